@@ -1,0 +1,238 @@
+"""ctypes binding of libcp_attn.so (the C ABI in include/cp_attn.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and contiguity, then
+their device pointers and torch's current HIP stream are handed to the library. Every step of
+the computation runs in the library's kernels. If the library has not been built this module
+raises on first use; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcp_attn.so")
+
+CP_OK, CP_STEP_SKIPPED = 0, 1
+CP_F32, CP_BF16 = 0, 1
+
+
+class CpAttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
+                ("len_q", ctypes.c_int32), ("len_kv", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("q_pos0", ctypes.c_int64), ("kv_pos0", ctypes.c_int64),
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("accumulate", ctypes.c_int32)]
+
+
+class RingDesc(ctypes.Structure):
+    _fields_ = [("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
+                ("chunk_len", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("n_cp", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libcp_attn.so (built in-tree); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it first "
+                           "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(_LIB_PATH)
+    st = ctypes.c_int32
+    lib.cp_attn_step.argtypes = [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P]
+    lib.cp_attn_step.restype = st
+    lib.cp_attn_merge.argtypes = [ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P, _P]
+    lib.cp_attn_merge.restype = st
+    lib.cp_attn_bwd_prep.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P]
+    lib.cp_attn_bwd_prep.restype = st
+    lib.cp_attn_bwd.argtypes = [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.cp_attn_bwd.restype = st
+    lib.cp_ring_schedule.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    lib.cp_ring_schedule.restype = ctypes.c_int32
+    lib.cp_attn_ring_fwd.argtypes = [ctypes.POINTER(RingDesc), _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.cp_attn_ring_fwd.restype = st
+    lib.cp_attn_ring_bwd.argtypes = [ctypes.POINTER(RingDesc), _P, _P, _P, _P, _P, _P, _P, _P,
+                                     _P, _P, _P]
+    lib.cp_attn_ring_bwd.restype = st
+    lib.cp_attn_status_string.argtypes = [ctypes.c_int32]
+    lib.cp_attn_status_string.restype = ctypes.c_char_p
+    lib.cp_attn_abi_version.argtypes = []
+    lib.cp_attn_abi_version.restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().cp_attn_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(load().cp_attn_abi_version())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    if t.dtype == torch.bfloat16:
+        return CP_BF16
+    if t.dtype == torch.float32:
+        return CP_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need(t, name, shape=None, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _check(status: int, what: str, allow_skip=True) -> int:
+    if status == CP_OK or (allow_skip and status == CP_STEP_SKIPPED):
+        return status
+    raise CpAttnError(status, what)
+
+
+def _desc(q, k, q_pos0, kv_pos0, causal, scale, accumulate):
+    hq, lq, d = q.shape
+    hkv, lk, _ = k.shape
+    return AttnDesc(hq, hkv, lq, lk, d, int(bool(causal)), int(q_pos0), int(kv_pos0),
+                    float(scale) if scale else 0.0, _dtype_code(q), int(bool(accumulate)))
+
+
+def step(q, k, v, o, lse, q_pos0=0, kv_pos0=0, causal=False, scale=None, accumulate=False):
+    """cp_attn_step: q [H_q, L_q, d]; k, v [H_kv, L_kv, d]; o [H_q, L_q, d] fp32; lse [H_q, L_q]
+    fp32. Returns CP_OK or CP_STEP_SKIPPED."""
+    _need(q, "q")
+    _need(k, "k", dtype=q.dtype)
+    _need(v, "v", shape=k.shape, dtype=q.dtype)
+    _need(o, "o", shape=q.shape, dtype=torch.float32)
+    _need(lse, "lse", shape=q.shape[:2], dtype=torch.float32)
+    d = _desc(q, k, q_pos0, kv_pos0, causal, scale, accumulate)
+    return _check(load().cp_attn_step(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                      _ptr(lse), _stream()), "cp_attn_step")
+
+
+def merge(o_acc, lse_acc, o, lse):
+    """cp_attn_merge (in place on o_acc, lse_acc)."""
+    _need(o_acc, "o_acc", dtype=torch.float32)
+    _need(lse_acc, "lse_acc", shape=o_acc.shape[:-1], dtype=torch.float32)
+    _need(o, "o", shape=o_acc.shape, dtype=torch.float32)
+    _need(lse, "lse", shape=lse_acc.shape, dtype=torch.float32)
+    rows = math.prod(o_acc.shape[:-1])
+    return _check(load().cp_attn_merge(rows, o_acc.shape[-1], _ptr(o_acc), _ptr(lse_acc), _ptr(o),
+                                       _ptr(lse), _stream()), "cp_attn_merge", allow_skip=False)
+
+
+def bwd_prep(o, d_o, delta):
+    """cp_attn_bwd_prep: delta = rowsum(dO * O)."""
+    _need(o, "o", dtype=torch.float32)
+    _need(d_o, "d_o", shape=o.shape)
+    _need(delta, "delta", shape=o.shape[:-1], dtype=torch.float32)
+    rows = math.prod(o.shape[:-1])
+    return _check(load().cp_attn_bwd_prep(rows, o.shape[-1], _dtype_code(d_o), _ptr(o), _ptr(d_o),
+                                          _ptr(delta), _stream()), "cp_attn_bwd_prep",
+                  allow_skip=False)
+
+
+def bwd(q, k, v, d_o, lse, delta, dq, dk, dv, q_pos0=0, kv_pos0=0, causal=False, scale=None):
+    """cp_attn_bwd: dq, dk, dv (fp32) are accumulated."""
+    _need(q, "q")
+    _need(k, "k", dtype=q.dtype)
+    _need(v, "v", shape=k.shape, dtype=q.dtype)
+    _need(d_o, "d_o", shape=q.shape, dtype=q.dtype)
+    _need(lse, "lse", shape=q.shape[:2], dtype=torch.float32)
+    _need(delta, "delta", shape=q.shape[:2], dtype=torch.float32)
+    _need(dq, "dq", shape=q.shape, dtype=torch.float32)
+    _need(dk, "dk", shape=k.shape, dtype=torch.float32)
+    _need(dv, "dv", shape=k.shape, dtype=torch.float32)
+    d = _desc(q, k, q_pos0, kv_pos0, causal, scale, False)
+    return _check(load().cp_attn_bwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(d_o),
+                                     _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv),
+                                     _stream()), "cp_attn_bwd")
+
+
+def ring_schedule(n_cp: int, rank: int, causal: bool):
+    """cp_ring_schedule: [(chunk, class)] for the n_cp steps (host only, no GPU needed)."""
+    chunks = (ctypes.c_int32 * max(n_cp, 1))()
+    classes = (ctypes.c_int32 * max(n_cp, 1))()
+    n = load().cp_ring_schedule(int(n_cp), int(rank), int(bool(causal)), chunks, classes)
+    if n < 0:
+        raise CpAttnError(n, "cp_ring_schedule")
+    return [(chunks[s], classes[s]) for s in range(n_cp)]
+
+
+def _ring(q, k_chunks, rank, causal, scale):
+    hq, lc, d = q.shape
+    n_cp, hkv = k_chunks.shape[0], k_chunks.shape[1]
+    return RingDesc(hq, hkv, lc, d, n_cp, int(rank), int(bool(causal)),
+                    float(scale) if scale else 0.0, _dtype_code(q))
+
+
+def ring_fwd(q, k_chunks, v_chunks, o, lse, rank, causal, scale=None, o_work=None, lse_work=None):
+    """cp_attn_ring_fwd: q [H_q, L_c, d]; k_chunks, v_chunks [N_cp, H_kv, L_c, d]."""
+    _need(q, "q")
+    n_cp, hkv, lc, d = k_chunks.shape
+    _need(k_chunks, "k_chunks", shape=(n_cp, hkv, q.shape[1], q.shape[2]), dtype=q.dtype)
+    _need(v_chunks, "v_chunks", shape=k_chunks.shape, dtype=q.dtype)
+    _need(o, "o", shape=q.shape, dtype=torch.float32)
+    _need(lse, "lse", shape=q.shape[:2], dtype=torch.float32)
+    if o_work is not None:
+        _need(o_work, "o_work", shape=q.shape, dtype=torch.float32)
+        _need(lse_work, "lse_work", shape=q.shape[:2], dtype=torch.float32)
+    r = _ring(q, k_chunks, rank, causal, scale)
+    return _check(load().cp_attn_ring_fwd(ctypes.byref(r), _ptr(q), _ptr(k_chunks), _ptr(v_chunks),
+                                          _ptr(o), _ptr(lse), _ptr(o_work), _ptr(lse_work),
+                                          _stream()), "cp_attn_ring_fwd", allow_skip=False)
+
+
+def ring_bwd(q, k_chunks, v_chunks, d_o, o, lse, delta_work, dq, dk_chunks, dv_chunks, rank,
+             causal, scale=None):
+    """cp_attn_ring_bwd: dq, dk_chunks, dv_chunks (fp32) are accumulated."""
+    _need(q, "q")
+    _need(k_chunks, "k_chunks", dtype=q.dtype)
+    _need(v_chunks, "v_chunks", shape=k_chunks.shape, dtype=q.dtype)
+    _need(d_o, "d_o", shape=q.shape, dtype=q.dtype)
+    _need(o, "o", shape=q.shape, dtype=torch.float32)
+    _need(lse, "lse", shape=q.shape[:2], dtype=torch.float32)
+    _need(delta_work, "delta_work", shape=q.shape[:2], dtype=torch.float32)
+    _need(dq, "dq", shape=q.shape, dtype=torch.float32)
+    _need(dk_chunks, "dk_chunks", shape=k_chunks.shape, dtype=torch.float32)
+    _need(dv_chunks, "dv_chunks", shape=k_chunks.shape, dtype=torch.float32)
+    r = _ring(q, k_chunks, rank, causal, scale)
+    return _check(load().cp_attn_ring_bwd(ctypes.byref(r), _ptr(q), _ptr(k_chunks), _ptr(v_chunks),
+                                          _ptr(d_o), _ptr(o), _ptr(lse), _ptr(delta_work), _ptr(dq),
+                                          _ptr(dk_chunks), _ptr(dv_chunks), _stream()),
+                  "cp_attn_ring_bwd", allow_skip=False)

@@ -1,0 +1,51 @@
+// Parameter blocks and launchers of the gfx950 kernels (internal to the library; the public
+// boundary is include/cp_attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cpa {
+
+struct StepParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* o;
+  float* lse;
+  int heads_q, heads_kv, group;
+  int len_q, len_kv, head_dim;
+  long long q_pos0, kv_pos0;
+  int causal;
+  int accumulate;
+  float scale;       // softmax scale
+  float scale_log2;  // scale * log2(e)
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* d_o;
+  const float* lse;
+  const float* delta;
+  float* dq;
+  float* dk;
+  float* dv;
+  int heads_q, heads_kv, group;
+  int len_q, len_kv, head_dim;
+  long long q_pos0, kv_pos0;
+  int causal;
+  float scale;
+  float scale_log2;
+};
+
+hipError_t launch_fwd_bf16(const StepParams& p, hipStream_t s);
+hipError_t launch_fwd_f32(const StepParams& p, hipStream_t s);
+hipError_t launch_merge(long long rows, int head_dim, float* o_acc, float* lse_acc,
+                        const float* o, const float* lse, hipStream_t s);
+hipError_t launch_bwd_prep(long long rows, int head_dim, int is_bf16, const float* o,
+                           const void* d_o, float* delta, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s);
+
+}  // namespace cpa

@@ -1,0 +1,213 @@
+"""Forward parity on the GPU: cp_attn_step, cp_attn_merge and the native ring driver against
+the fp64 oracle on the same seeded inputs, called through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_sequence_amd import binding as cp
+from long_context_sequence_amd import configs, inputs
+
+from util import (check_o_lse, device_inputs, host_inputs, oracle_rank, sample_rows,
+                  small_workload)
+
+pytestmark = pytest.mark.gpu
+
+
+def _ring_gpu(wl, rank, fused=True):
+    q, k, v = device_inputs(wl, rank)
+    o = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    ow = lw = None
+    if not fused:
+        ow, lw = torch.empty_like(o), torch.empty_like(lse)
+    cp.ring_fwd(q, k, v, o, lse, rank, wl.causal, o_work=ow, lse_work=lw)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), lse.cpu().numpy()
+
+
+def test_c1_tiny_noncausal_fp32_full():
+    wl = configs.C1
+    o, lse = _ring_gpu(wl, 0)
+    o_ref, lse_ref = oracle_rank(wl, 0)
+    check_o_lse(o, lse, o_ref, lse_ref, "f32", "C1")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("fused", [True, False])
+def test_small_ragged_gqa_all_ranks(d, causal, fused):
+    # 200-row chunks: one full 128-row query tile plus a ragged one, three 64-key tiles plus a
+    # ragged one; GQA group 2.
+    wl = small_workload(101, "bf16", 4, 2, d, 200, 3, causal)
+    for r in range(wl.n_cp):
+        o, lse = _ring_gpu(wl, r, fused)
+        o_ref, lse_ref = oracle_rank(wl, r)
+        check_o_lse(o, lse, o_ref, lse_ref, "bf16", f"rank {r}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("q0,k0,causal,accumulate", [
+    (0, 0, True, False),      # diagonal
+    (500, 0, True, False),    # fully visible
+    (0, 0, False, False),
+    (40, 100, True, False),   # rows before position 100 see nothing
+    (300, 250, True, True),   # fold into an existing running result
+    (0, 0, False, True),
+])
+def test_single_step_offsets(dtype, q0, k0, causal, accumulate):
+    hq, hkv, d, lq, lk = 6, 2, 128, 150, 170
+    torch_dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    qa = inputs.make(102, "q", 0, (hq, lq, d), dtype)
+    ka = inputs.make(102, "k", 0, (hkv, lk, d), dtype)
+    va = inputs.make(102, "v", 0, (hkv, lk, d), dtype)
+    q, k, v = (inputs.to_torch(a, "cuda") for a in (qa, ka, va))
+    assert q.dtype == torch_dt
+    o_ref, lse_ref = oracle.attention_forward(inputs.widen(qa), inputs.widen(ka), inputs.widen(va),
+                                              q_pos0=q0, kv_pos0=k0, causal=causal)
+    if accumulate:
+        # running result over a disjoint key set (the previous chunk), then fold this step in
+        kp = inputs.make(102, "k", 1, (hkv, lk, d), dtype)
+        vp = inputs.make(102, "v", 1, (hkv, lk, d), dtype)
+        prev_o, prev_l = oracle.attention_forward(inputs.widen(qa), inputs.widen(kp),
+                                                  inputs.widen(vp), q_pos0=q0, kv_pos0=k0 - lk,
+                                                  causal=causal)
+        o = torch.from_numpy(prev_o.astype(np.float32)).cuda()
+        lse = torch.from_numpy(prev_l.astype(np.float32)).cuda()
+        o_ref, lse_ref = oracle.merge(prev_o, prev_l, o_ref, lse_ref)
+    else:
+        o = torch.full((hq, lq, d), 7.0, device="cuda")
+        lse = torch.full((hq, lq), 7.0, device="cuda")
+    st = cp.step(q, k, v, o, lse, q_pos0=q0, kv_pos0=k0, causal=causal, accumulate=accumulate)
+    assert st == cp.CP_OK
+    torch.cuda.synchronize()
+    check_o_lse(o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, dtype, "step")
+
+
+def test_step_skipped_writes_nothing():
+    q = torch.zeros(2, 64, 128, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(2, 64, 128, dtype=torch.bfloat16, device="cuda")
+    o = torch.full((2, 64, 128), 3.0, device="cuda")
+    lse = torch.full((2, 64), 3.0, device="cuda")
+    st = cp.step(q, k, k, o, lse, q_pos0=0, kv_pos0=64, causal=True)
+    torch.cuda.synchronize()
+    assert st == cp.CP_STEP_SKIPPED
+    assert bool((o == 3.0).all()) and bool((lse == 3.0).all())
+
+
+def test_empty_chunk_gives_zero_and_neg_inf():
+    q = torch.randn(2, 10, 64, device="cuda").to(torch.bfloat16)
+    k = torch.zeros(2, 0, 64, dtype=torch.bfloat16, device="cuda")
+    o = torch.full((2, 10, 64), 3.0, device="cuda")
+    lse = torch.full((2, 10), 3.0, device="cuda")
+    assert cp.step(q, k, k, o, lse) == cp.CP_OK
+    torch.cuda.synchronize()
+    assert bool((o == 0).all()) and bool(torch.isneginf(lse).all())
+
+
+def test_single_visible_key_closed_form():
+    wl = small_workload(103, "bf16", 2, 2, 128, 96, 2, True)
+    qa, ka, va = (inputs.workload_tensor(wl, "q", 0), inputs.workload_kv(wl, "k"),
+                  inputs.workload_kv(wl, "v"))
+    q, k, v = (inputs.to_torch(a, "cuda") for a in (qa, ka, va))
+    o = torch.empty(q.shape, device="cuda")
+    lse = torch.empty(q.shape[:2], device="cuda")
+    cp.ring_fwd(q, k, v, o, lse, 0, True)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    # query 0 of rank 0 sees key 0 only: O = v_0 exactly, LSE = scale * q_0 . k_0
+    qh, kh, vh = inputs.widen(qa), inputs.widen(ka), inputs.widen(va)
+    for h in range(2):
+        assert np.array_equal(o[h, 0], vh[0, h, 0].astype(np.float32))
+        assert abs(lse[h, 0] - qh[h, 0] @ kh[0, h, 0] / np.sqrt(128)) < 1e-5
+
+
+def test_constant_v_gives_constant_output():
+    wl = small_workload(106, "bf16", 4, 2, 128, 200, 3, True)
+    q, k, _ = device_inputs(wl, 2)
+    v = torch.full(k.shape, 0.375, dtype=torch.bfloat16, device="cuda")
+    o = torch.empty(q.shape, device="cuda")
+    lse = torch.empty(q.shape[:2], device="cuda")
+    cp.ring_fwd(q, k, v, o, lse, 2, True)
+    torch.cuda.synchronize()
+    # O = c * sum(bf16(P)) / sum(P): only the rounding of P (relative 2^-9) separates it from c
+    assert float((o - 0.375).abs().max()) <= 0.375 * 2 ** -8
+
+
+def test_merge_kernel_against_oracle():
+    rng = np.random.default_rng(5)
+    hq, lq, d = 3, 77, 128
+    oa, ob = rng.standard_normal((hq, lq, d)), rng.standard_normal((hq, lq, d))
+    la, lb = rng.standard_normal((hq, lq)) * 3, rng.standard_normal((hq, lq)) * 3
+    la[0, :5] = -np.inf
+    lb[0, 3:8] = -np.inf
+    oa[0, :5] = 0
+    ob[0, 3:8] = 0
+    ref_o, ref_l = oracle.merge(oa, la, ob, lb)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()  # noqa
+    o_acc, l_acc, o, l = t(oa), t(la), t(ob), t(lb)
+    cp.merge(o_acc, l_acc, o, l)
+    torch.cuda.synchronize()
+    got_o, got_l = o_acc.cpu().numpy(), l_acc.cpu().numpy()
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(ref_l))
+    fin = np.isfinite(ref_l)
+    assert np.max(np.abs(got_l[fin] - ref_l[fin])) < 1e-5
+    assert np.max(np.abs(got_o - ref_o)) < 1e-5
+
+
+def test_bwd_prep_equals_softmax_jacobian_term():
+    wl = small_workload(104, "bf16", 4, 2, 128, 160, 2, True)
+    r = 1
+    qh, kh, vh, doh = host_inputs(wl, r, with_do=True)
+    q, k, v, d_o = device_inputs(wl, r, with_do=True)
+    o = torch.empty(q.shape, device="cuda")
+    lse = torch.empty(q.shape[:2], device="cuda")
+    cp.ring_fwd(q, k, v, o, lse, r, True)
+    delta = torch.empty(q.shape[:2], device="cuda")
+    cp.bwd_prep(o, d_o, delta)
+    torch.cuda.synchronize()
+    kf = np.concatenate(list(kh), axis=1)
+    vf = np.concatenate(list(vh), axis=1)
+    ref = oracle.softmax_dot(qh, kf, vf, doh, q_pos0=r * wl.chunk_len, causal=True)
+    assert np.max(np.abs(delta.cpu().numpy() - ref)) < 2e-2 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_forward_is_deterministic():
+    wl = small_workload(105, "bf16", 8, 2, 128, 512, 4, True)
+    a = _ring_gpu(wl, 3)
+    b = _ring_gpu(wl, 3)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("key", [2, 3, 4])
+def test_full_size_sampled_rows(key):
+    """The named workloads at full size, in the launch configuration the benchmark times, on
+    sampled rows the oracle computes one by one; plus rows-sum-to-one with the GPU's LSE."""
+    wl = configs.WORKLOADS[key]
+    ranks = (0, 3, 7) if key == 2 else wl.ranks
+    k_host = inputs.workload_kv(wl, "k")
+    v_host = inputs.workload_kv(wl, "v")
+    kd, vd = inputs.to_torch(k_host, "cuda"), inputs.to_torch(v_host, "cuda")
+    kf = np.concatenate([inputs.bf16_bits_to_f32(c) for c in k_host], axis=1)
+    vf = np.concatenate([inputs.bf16_bits_to_f32(c) for c in v_host], axis=1)
+    for r in ranks:
+        qa = inputs.workload_tensor(wl, "q", r)
+        q = inputs.to_torch(qa, "cuda")
+        o = torch.empty(q.shape, device="cuda")
+        lse = torch.empty(q.shape[:2], device="cuda")
+        cp.ring_fwd(q, kd, vd, o, lse, r, wl.causal)
+        torch.cuda.synchronize()
+        heads, rows = sample_rows(wl, r, 24, seed=key * 100 + r)
+        o_s = o[heads, rows].cpu().numpy()
+        l_s = lse[heads, rows].cpu().numpy()
+        qf = inputs.widen(qa)[heads, rows]
+        o_ref, l_ref = oracle.attention_rows(qf, kf, vf, heads, rows, wl.heads_q,
+                                             q_pos0=r * wl.chunk_len, causal=wl.causal,
+                                             scale=wl.scale)
+        check_o_lse(o_s, l_s, o_ref, l_ref, "bf16", f"C{key} rank {r}")
+        # rows sum to one with the GPU's LSE: sum_j exp(s_ij - LSE_i) = 1 (fp64 scores)
+        g = heads // wl.group
+        for t in range(4):
+            nvis = r * wl.chunk_len + rows[t] + 1 if wl.causal else wl.seq_len
+            s = (kf[g[t], :nvis].astype(np.float64) @ qf[t]) * wl.scale
+            assert abs(np.sum(np.exp(s - l_s[t])) - 1.0) < 2e-3
