@@ -1,0 +1,287 @@
+"""Throughput of one context-parallel rank's ring attention on one MI355X.
+
+A timed step is one pass of the rank's whole hot path over its synthetic inputs: the forward
+ring (every visited chunk: the step kernel folding into the running (O, LSE)) and, when the
+workload has one, the backward ring (delta prep, then the backward kernels per visited chunk,
+into zeroed fp32 dQ/dK/dV). Inputs are resident in HBM before the timed region starts.
+
+Default workload: rank 15 of a 212,992-token sequence in 16 chunks of 13,312 (32 query heads,
+8 key/value heads, d = 128, causal), forward + backward.
+
+Prints one JSON line. `value` is fwd+bwd algorithmic TFLOP/s (visible query-key pairs only:
+4*d*H_q flops per pair forward, 10*d*H_q backward); the forward and backward rates, tokens/s and
+the per-kernel roofline ride along. HIP events recorded on the launch stream around every step
+kernel inside the timed region give the per-kernel durations.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=4, help="named workload key (2..5)")
+    ap.add_argument("--rank", type=int, default=None)
+    ap.add_argument("--fwd-only", action="store_true")
+    ap.add_argument("--separate-merge", action="store_true",
+                    help="step into scratch + cp_attn_merge instead of the fused fold")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of the oracle CPU baseline (0 disables it)")
+    ap.add_argument("--merge-bench", action="store_true", default=True)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs one rank's ring on one GPU; "
+                                   "multi-GPU runs are not supported (use --gpus 1)"}))
+        sys.exit(2)
+    import torch
+
+    from long_context_sequence_amd import binding as cp
+    from long_context_sequence_amd import configs, inputs
+
+    wl = configs.WORKLOADS[args.workload]
+    rank = wl.ranks[-1] if args.rank is None else args.rank
+    do_bwd = not args.fwd_only
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    cp.load()
+
+    t0 = time.time()
+    q = inputs.to_torch(inputs.workload_tensor(wl, "q", rank), dev)
+    kc = inputs.to_torch(inputs.workload_kv(wl, "k"), dev)
+    vc = inputs.to_torch(inputs.workload_kv(wl, "v"), dev)
+    d_o = inputs.to_torch(inputs.workload_tensor(wl, "do", rank), dev)
+    print(f"# inputs ready in {time.time() - t0:.1f}s: q {tuple(q.shape)} kv {tuple(kc.shape)}",
+          file=sys.stderr, flush=True)
+    hq, lc, d = q.shape
+    o = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    o_work = torch.empty_like(o) if args.separate_merge else None
+    lse_work = torch.empty_like(lse) if args.separate_merge else None
+    delta = torch.empty_like(lse)
+    dq = torch.zeros_like(o)
+    dk = torch.zeros(kc.shape, dtype=torch.float32, device=dev)
+    dv = torch.zeros(kc.shape, dtype=torch.float32, device=dev)
+
+    sched = [(c, cls) for c, cls in cp.ring_schedule(wl.n_cp, rank, wl.causal)
+             if cls != configs.SKIP]
+
+    def step_flops(c):
+        # visible pairs per head of this chunk for this rank
+        if not wl.causal or c < rank:
+            return lc * lc
+        return lc * (lc + 1) // 2
+
+    fwd_step_flops = [4.0 * d * hq * step_flops(c) for c, _ in sched]
+    bwd_step_flops = [10.0 * d * hq * step_flops(c) for c, _ in sched]
+
+    # probe once whether the backward kernels exist in this build
+    if do_bwd:
+        try:
+            cp.bwd(q, kc[rank], vc[rank], d_o, lse, delta, dq, dk[rank], dv[rank],
+                   q_pos0=rank * lc, kv_pos0=rank * lc, causal=wl.causal)
+        except cp.CpAttnError as e:
+            if e.status != -5:
+                raise
+            do_bwd = False
+            print("# backward kernels not in this build: timing the forward only",
+                  file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+
+    def run_step(ev_f=None, ev_b=None):
+        first = True
+        for i, (c, _) in enumerate(sched):
+            if ev_f is not None:
+                ev_f[i][0].record(stream)
+            if first or not args.separate_merge:
+                cp.step(q, kc[c], vc[c], o, lse, q_pos0=rank * lc, kv_pos0=c * lc,
+                        causal=wl.causal, accumulate=not first)
+            else:
+                cp.step(q, kc[c], vc[c], o_work, lse_work, q_pos0=rank * lc, kv_pos0=c * lc,
+                        causal=wl.causal)
+            if ev_f is not None:
+                ev_f[i][1].record(stream)
+            if not first and args.separate_merge:
+                cp.merge(o, lse, o_work, lse_work)
+            first = False
+        if do_bwd:
+            dq.zero_()
+            dk.zero_()
+            dv.zero_()
+            cp.bwd_prep(o, d_o, delta)
+            for i, (c, _) in enumerate(sched):
+                if ev_b is not None:
+                    ev_b[i][0].record(stream)
+                cp.bwd(q, kc[c], vc[c], d_o, lse, delta, dq, dk[c], dv[c], q_pos0=rank * lc,
+                       kv_pos0=c * lc, causal=wl.causal)
+                if ev_b is not None:
+                    ev_b[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    evs_f = [[(mk(), mk()) for _ in sched] for _ in range(args.steps)]
+    evs_b = [[(mk(), mk()) for _ in sched] for _ in range(args.steps)]
+    start, end = mk(), mk()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(args.steps):
+        run_step(evs_f[s], evs_b[s] if do_bwd else None)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    fwd_ms = sum(a.elapsed_time(b) for st in evs_f for a, b in st) / args.steps
+    bwd_ms = (sum(a.elapsed_time(b) for st in evs_b for a, b in st) / args.steps) if do_bwd else 0.0
+    f_fwd = sum(fwd_step_flops)
+    f_bwd = sum(bwd_step_flops) if do_bwd else 0.0
+    print(f"# timed {args.steps} steps: {ms_step:.2f} ms/step (fwd kernels {fwd_ms:.2f} ms, "
+          f"bwd kernels {bwd_ms:.2f} ms)", file=sys.stderr, flush=True)
+
+    # dominant kernel: the one with the larger share of the step
+    if do_bwd and bwd_ms > fwd_ms:
+        dom_name, dom_ms, dom_flops, n_launch = "cp_attn_bwd", bwd_ms, f_bwd, len(sched)
+    else:
+        dom_name, dom_ms, dom_flops, n_launch = "cp_attn_step (fwd_bf16_kernel)", fwd_ms, f_fwd, len(sched)
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom_name, "achieved": round(achieved, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "launches_per_step": n_launch,
+                "avg_launch_ms": round(dom_ms / n_launch, 4)}
+
+    merge_info = None
+    if args.merge_bench:
+        merge_info = bench_merge(cp, torch, o, lse)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(wl, rank, args.cpu_seconds, do_bwd)
+
+    value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+    out = {
+        "metric": "ring-step causal attention TFLOP/s (fwd+bwd) per rank",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) bf16 Q/K/V/dO",
+        "config": {"workload": wl.name, "seq_len": wl.seq_len, "n_cp": wl.n_cp, "rank": rank,
+                   "chunk_len": lc, "heads_q": hq, "heads_kv": wl.heads_kv, "head_dim": d,
+                   "causal": wl.causal, "backward": do_bwd,
+                   "merge": "separate" if args.separate_merge else "fused"},
+        "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
+        "fwd_frac_of_peak": round(f_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2) if do_bwd else None,
+        "bwd_frac_of_peak": (round(f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+                             if do_bwd else None),
+        "tokens_per_s": round(lc / (ms_step * 1e-3), 1),
+        "roofline": roofline,
+        "merge_kernel": merge_info,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_merge(cp, torch, o, lse):
+    """cp_attn_merge alone on the rank's (O, LSE) shapes: GB/s of algorithmic traffic
+    (read O_acc, O_step, both LSEs; write O_acc, LSE_acc: 12 B per O element + 12 B per row)."""
+    o2 = torch.randn_like(o)
+    l2 = torch.randn_like(lse)
+    oa = torch.randn_like(o)
+    la = torch.randn_like(lse)
+    for _ in range(2):
+        cp.merge(oa, la, o2, l2)
+    torch.cuda.synchronize()
+    n = 10
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(n):
+        cp.merge(oa, la, o2, l2)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / n
+    byts = 12.0 * o.numel() + 12.0 * lse.numel()
+    gbs = byts / (ms * 1e-3) / 1e9
+    return {"avg_launch_ms": round(ms, 4), "bytes_per_launch": int(byts),
+            "achieved_GBs": round(gbs, 1), "peak_GBs": PEAK_HBM_GBS,
+            "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def cpu_baseline(wl, rank, budget_s, with_bwd):
+    """The fp64 oracle on the host cores, on a bounded sample of the same workload: blocks of
+    256 consecutive query rows of one head each, every row against all its visible keys
+    (forward, and the backward of those rows), until the time budget is used."""
+    import oracle
+    from long_context_sequence_amd import inputs
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    lc, d = wl.chunk_len, wl.head_dim
+    rows_per_block = 256
+    rng = np.random.default_rng(0)
+    qa = inputs.workload_tensor(wl, "q", rank)
+    da = inputs.workload_tensor(wl, "do", rank)
+    # one key/value head (and its group of query heads) for the whole sample
+    g = int(rng.integers(0, wl.heads_kv))
+    kf = np.concatenate([inputs.widen(inputs.workload_tensor(wl, "k", c)[g:g + 1])
+                         for c in range(wl.n_cp)], axis=1)
+    vf = np.concatenate([inputs.widen(inputs.workload_tensor(wl, "v", c)[g:g + 1])
+                         for c in range(wl.n_cp)], axis=1)
+    t_total = 0.0
+    flops = 0.0
+    blocks = 0
+    t_start = time.time()
+    while blocks == 0 or time.time() - t_start < budget_s:
+        h = g * wl.group + int(rng.integers(0, wl.group))
+        i0 = int(rng.integers(0, max(1, lc - rows_per_block)))
+        qb = inputs.widen(qa[h:h + 1, i0:i0 + rows_per_block])
+        db = inputs.widen(da[h:h + 1, i0:i0 + rows_per_block])
+        q0 = rank * lc + i0
+        nkeys = kf.shape[1]
+        pairs = sum(min(nkeys, q0 + i + 1) if wl.causal else nkeys for i in range(qb.shape[1]))
+        t = time.time()
+        oracle.attention_forward(qb, kf, vf, q_pos0=q0, causal=wl.causal, scale=wl.scale)
+        if with_bwd:
+            oracle.attention_backward(qb, kf, vf, db, q_pos0=q0, causal=wl.causal,
+                                      scale=wl.scale)
+        t_total += time.time() - t
+        flops += (14.0 if with_bwd else 4.0) * d * pairs
+        blocks += 1
+    return {"value": round(flops / t_total / 1e12, 5), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{blocks} blocks of {rows_per_block} query rows x all visible keys "
+                      f"({'fwd+bwd' if with_bwd else 'fwd'}, fp64 numpy, {t_total:.1f}s)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,6 +1,359 @@
-// Backward ring step (bf16): not implemented yet.
+// One ring step of the backward (bf16 MFMA, fp32 accumulate): the gradient of
+// loss = sum(O * dO) restricted to one key/value chunk, with P recomputed from the final
+// forward LSE (P = exp(s - LSE)) rather than stored, and delta = rowsum(dO * O) from the prep
+// kernel standing in for sum_j P_ij dP_ij.
+//
+// Two kernels, no atomics (every output element has one owner workgroup):
+//  * dkdv: a workgroup owns 128 keys of one key/value head (32 per wave, held in registers as
+//    MFMA operands) and streams the query tiles of every query head of its group through LDS:
+//      S = Q K^T, P = exp2(S*scale*log2e - LSE*log2e), dP = dO V^T, dS = P (dP - delta),
+//      dV^T += dO^T P,  dK^T += Q^T dS     (the group's heads summed in registers).
+//  * dq: a workgroup owns 128 query rows of one head (32 per wave) and streams key/value tiles:
+//      S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T.
+// Transposed operands (dO^T, Q^T, K^T) come from the same row-major LDS tiles through the
+// LDS transpose read. Outputs are accumulated (+=) into fp32 dQ, dK, dV.
+#include <math.h>
+
+#include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace cpa {
-hipError_t launch_bwd_bf16(const BwdParams&, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+constexpr int kQT = 64;    // query rows per tile (dkdv)
+constexpr int kKT = 64;    // keys per tile (dq)
+constexpr int kNW = 4;     // waves per workgroup
+constexpr int kNT = 64 * kNW;
+
+// Stage a rows x D bf16 tile (rows from `row0`, zero past `nrows`) into registers; then LDS.
+template <int D, int ROWS>
+struct TileStager {
+  static constexpr int CH = D / 8;
+  static constexpr int LD = ROWS * CH / kNT;
+  static_assert(ROWS * CH % kNT == 0, "tile must split evenly over the threads");
+  u32x4_t r[LD];
+  __device__ __forceinline__ void load(const uint16_t* src, int row0, int nrows, int tid) {
+#pragma unroll
+    for (int u = 0; u < LD; ++u) {
+      const int idx = tid + u * kNT;
+      const int rr = idx / CH, c = idx % CH;
+      const int row = row0 + rr;
+      const bool ok = row < nrows;
+      const int rc = ok ? row : nrows - 1;
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(src + (size_t)rc * D + 8 * c);
+      r[u] = ok ? x : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* dst, int tid) const {
+#pragma unroll
+    for (int u = 0; u < LD; ++u) {
+      const int idx = tid + u * kNT;
+      const int rr = idx / CH, c = idx % CH;
+      *reinterpret_cast<u32x4_t*>(dst + tile_off<D>(rr, c)) = r[u];
+    }
+  }
+};
+
+template <int D>
+__global__ void __launch_bounds__(kNT, 1) bwd_dkdv_kernel(BwdParams p) {
+  constexpr int KS = D / 16, NB = D / 32, BNK = 32 * kNW;
+  __shared__ __attribute__((aligned(16))) uint16_t sq[2][kQT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sdo[2][kQT * D];
+  __shared__ __attribute__((aligned(16))) float slse[2][kQT];
+  __shared__ __attribute__((aligned(16))) float sdel[2][kQT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
+  const int n_kt = (p.len_kv + BNK - 1) / BNK;
+  const int w = xcd_remap(blockIdx.x, n_kt * p.heads_kv);
+  const int g = w / n_kt;
+  const int kt = w % n_kt;  // ascending: under causality the earliest keys have most work
+  const int kv_base = kt * BNK;
+
+  // This lane's key: column of the S = Q K^T and dP = dO V^T products.
+  const int key = kv_base + 32 * wave + col;
+  const bool k_ok = key < p.len_kv;
+  const int key_c = k_ok ? key : p.len_kv - 1;
+  const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (size_t)g * p.len_kv * D;
+  const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (size_t)g * p.len_kv * D;
+  u32x4_t kb[KS], vb[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const u32x4_t xk = *reinterpret_cast<const u32x4_t*>(kg + (size_t)key_c * D + 16 * ks + 8 * half);
+    const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(vg + (size_t)key_c * D + 16 * ks + 8 * half);
+    kb[ks] = k_ok ? xk : u32x4_t{0u, 0u, 0u, 0u};
+    vb[ks] = k_ok ? xv : u32x4_t{0u, 0u, 0u, 0u};
+  }
+
+  // Query tiles that see at least one key of this workgroup.
+  int qt_first = 0;
+  if (p.causal) {
+    const long long first_row = p.kv_pos0 + kv_base - p.q_pos0;
+    qt_first = first_row <= 0 ? 0 : (int)min<long long>(first_row / kQT, (p.len_q + kQT - 1) / kQT);
+  }
+  const int n_qt = (p.len_q + kQT - 1) / kQT;
+  const int per_head = n_qt - qt_first;
+  const int n_it = per_head * p.group;
+
+  f32x16_t dkt[NB], dvt[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    dkt[nb] = f32x16_t{};
+    dvt[nb] = f32x16_t{};
+  }
+
+  TileStager<D, kQT> stq, stdo;
+  float st_lse = 0.f, st_del = 0.f;
+  auto load_it = [&](int it) {
+    const int h = g * p.group + it / per_head;
+    const int q0 = (qt_first + it % per_head) * kQT;
+    const uint16_t* qh = static_cast<const uint16_t*>(p.q) + (size_t)h * p.len_q * D;
+    const uint16_t* doh = static_cast<const uint16_t*>(p.d_o) + (size_t)h * p.len_q * D;
+    stq.load(qh, q0, p.len_q, tid);
+    stdo.load(doh, q0, p.len_q, tid);
+    if (tid < kQT) {
+      const int row = q0 + tid;
+      const bool ok = row < p.len_q;
+      const float l = ok ? p.lse[(size_t)h * p.len_q + row] : -INFINITY;
+      // rows past the end or with no visible key anywhere get P = 0
+      st_lse = l == -INFINITY ? INFINITY : l * kLog2e;
+    } else if (tid < 2 * kQT) {
+      const int row = q0 + tid - kQT;
+      st_del = row < p.len_q ? p.delta[(size_t)h * p.len_q + row] : 0.f;
+    }
+  };
+  auto store_it = [&](int buf) {
+    stq.store(sq[buf], tid);
+    stdo.store(sdo[buf], tid);
+    if (tid < kQT) slse[buf][tid] = st_lse;
+    else if (tid < 2 * kQT) sdel[buf][tid - kQT] = st_del;
+  };
+
+  if (n_it > 0) {
+    load_it(0);
+    store_it(0);
+  }
+  __syncthreads();
+
+  const float c2 = p.scale_log2;
+  const long long key_pos = p.kv_pos0 + key;                    // this lane's key position
+  const long long wave_k0 = p.kv_pos0 + kv_base + 32 * wave;   // first key position of the wave
+
+  for (int it = 0; it < n_it; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < n_it) load_it(it + 1);
+    const int q0 = (qt_first + it % per_head) * kQT;
+    const long long qpos0 = p.q_pos0 + q0;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const long long bpos = qpos0 + 32 * b;  // position of the block's first row
+      if (p.causal && bpos + 31 < wave_k0) continue;  // no row of the block sees the wave's keys
+      const bool need_mask = p.causal && bpos < wave_k0 + 31;
+      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+      const int arow = 32 * b + perm_row(col);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        s = mfma32x32x16(tile_row8<D>(sq[buf], arow, 2 * ks + half), kb[ks], s);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        dp = mfma32x32x16(tile_row8<D>(sdo[buf], arow, 2 * ks + half), vb[ks], dp);
+      u32x4_t pb[2], dsb[2];
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        // accumulator registers 4*a4 .. 4*a4+3 hold 4 consecutive query rows of the tile
+        const int rbase = 32 * b + 16 * (a4 >> 1) + 8 * half + 4 * (a4 & 1);
+        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(&slse[buf][rbase]);
+        const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&sdel[buf][rbase]);
+        float pv[4], dsv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * a4 + e], c2, -l4[e]));
+          if (need_mask && key_pos > qpos0 + rbase + e) pr = 0.f;
+          pv[e] = pr;
+          dsv[e] = pr * (dp[4 * a4 + e] - d4[e]);
+        }
+        pb[a4 >> 1][2 * (a4 & 1)] = pack_bf16x2(pv[0], pv[1]);
+        pb[a4 >> 1][2 * (a4 & 1) + 1] = pack_bf16x2(pv[2], pv[3]);
+        dsb[a4 >> 1][2 * (a4 & 1)] = pack_bf16x2(dsv[0], dsv[1]);
+        dsb[a4 >> 1][2 * (a4 & 1) + 1] = pack_bf16x2(dsv[2], dsv[3]);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          dvt[nb] = mfma32x32x16(tile_col8<D>(sdo[buf], 32 * b + 16 * q, 32 * nb, lane), pb[q], dvt[nb]);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          dkt[nb] = mfma32x32x16(tile_col8<D>(sq[buf], 32 * b + 16 * q, 32 * nb, lane), dsb[q], dkt[nb]);
+    }
+    if (it + 1 < n_it) store_it(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!k_ok) return;
+  float* dkr = p.dk + ((size_t)g * p.len_kv + key) * D;
+  float* dvr = p.dv + ((size_t)g * p.len_kv + key) * D;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int n = 32 * nb + 8 * a4 + 4 * half;
+      f32x4_t* pk = reinterpret_cast<f32x4_t*>(dkr + n);
+      f32x4_t* pv = reinterpret_cast<f32x4_t*>(dvr + n);
+      f32x4_t ok4 = *pk, ov4 = *pv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ok4[e] += p.scale * dkt[nb][4 * a4 + e];
+        ov4[e] += dvt[nb][4 * a4 + e];
+      }
+      *pk = ok4;
+      *pv = ov4;
+    }
+}
+
+template <int D>
+__global__ void __launch_bounds__(kNT, 1) bwd_dq_kernel(BwdParams p) {
+  constexpr int KS = D / 16, NB = D / 32, BM = 32 * kNW;
+  __shared__ __attribute__((aligned(16))) uint16_t sk[2][kKT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[2][kKT * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
+  const int n_qt = (p.len_q + BM - 1) / BM;
+  const int w = xcd_remap(blockIdx.x, n_qt * p.heads_q);
+  const int h_in = w % p.group;
+  const int rest = w / p.group;
+  const int qt = n_qt - 1 - rest % n_qt;  // causally longest tiles first
+  const int g = rest / n_qt;
+  const int h = g * p.group + h_in;
+  const int q_base = qt * BM;
+
+  const int qi = q_base + 32 * wave + col;
+  const bool q_ok = qi < p.len_q;
+  const int qi_c = q_ok ? qi : p.len_q - 1;
+  const uint16_t* qh = static_cast<const uint16_t*>(p.q) + (size_t)h * p.len_q * D;
+  const uint16_t* doh = static_cast<const uint16_t*>(p.d_o) + (size_t)h * p.len_q * D;
+  u32x4_t qb[KS], dob[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const u32x4_t xq = *reinterpret_cast<const u32x4_t*>(qh + (size_t)qi_c * D + 16 * ks + 8 * half);
+    const u32x4_t xd = *reinterpret_cast<const u32x4_t*>(doh + (size_t)qi_c * D + 16 * ks + 8 * half);
+    qb[ks] = q_ok ? xq : u32x4_t{0u, 0u, 0u, 0u};
+    dob[ks] = q_ok ? xd : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  const float lse_raw = q_ok ? p.lse[(size_t)h * p.len_q + qi] : -INFINITY;
+  const float lse2 = lse_raw == -INFINITY ? INFINITY : lse_raw * kLog2e;
+  const float del = q_ok ? p.delta[(size_t)h * p.len_q + qi] : 0.f;
+
+  const int last_row = min(q_base + BM, p.len_q) - 1;
+  long long nk = p.len_kv;
+  if (p.causal) nk = min(nk, p.q_pos0 + last_row - p.kv_pos0 + 1);
+  const int n_kt = nk > 0 ? (int)((nk + kKT - 1) / kKT) : 0;
+
+  const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (size_t)g * p.len_kv * D;
+  const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (size_t)g * p.len_kv * D;
+  TileStager<D, kKT> stk, stv;
+
+  f32x16_t dqt[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) dqt[nb] = f32x16_t{};
+
+  if (n_kt > 0) {
+    stk.load(kg, 0, p.len_kv, tid);
+    stv.load(vg, 0, p.len_kv, tid);
+    stk.store(sk[0], tid);
+    stv.store(sv[0], tid);
+  }
+  __syncthreads();
+
+  const float c2 = p.scale_log2;
+  const long long wave_q0 = p.q_pos0 + q_base + 32 * wave;
+  const long long qpos = wave_q0 + col;
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < n_kt) {
+      stk.load(kg, (kt + 1) * kKT, p.len_kv, tid);
+      stv.load(vg, (kt + 1) * kKT, p.len_kv, tid);
+    }
+    const long long key_pos0 = p.kv_pos0 + (long long)kt * kKT;
+    const bool wave_visible = !p.causal || key_pos0 <= wave_q0 + 31;
+    if (wave_visible) {
+      const bool need_mask =
+          (kt * kKT + kKT > p.len_kv) || (p.causal && key_pos0 + kKT - 1 > wave_q0);
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+        const int arow = 32 * blk + perm_row(col);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          s = mfma32x32x16(tile_row8<D>(sk[buf], arow, 2 * ks + half), qb[ks], s);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          dp = mfma32x32x16(tile_row8<D>(sv[buf], arow, 2 * ks + half), dob[ks], dp);
+        u32x4_t dsb[2];
+#pragma unroll
+        for (int r2 = 0; r2 < 8; ++r2) {
+          float dsv[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int r = 2 * r2 + e;
+            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -lse2));
+            if (need_mask) {
+              const int kk = kt * kKT + 32 * blk + perm_row(8 * (r >> 2) + 4 * half + (r & 3));
+              if (kk >= p.len_kv || (p.causal && p.kv_pos0 + kk > qpos)) pr = 0.f;
+            }
+            dsv[e] = pr * (dp[r] - del);
+          }
+          dsb[r2 >> 2][r2 & 3] = pack_bf16x2(dsv[0], dsv[1]);
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+            dqt[nb] = mfma32x32x16(tile_col8<D>(sk[buf], 32 * blk + 16 * q, 32 * nb, lane), dsb[q], dqt[nb]);
+      }
+    }
+    if (kt + 1 < n_kt) {
+      stk.store(sk[buf ^ 1], tid);
+      stv.store(sv[buf ^ 1], tid);
+    }
+    __syncthreads();
+  }
+
+  if (!q_ok) return;
+  float* dqr = p.dq + ((size_t)h * p.len_q + qi) * D;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      f32x4_t* ptr = reinterpret_cast<f32x4_t*>(dqr + 32 * nb + 8 * a4 + 4 * half);
+      f32x4_t o4 = *ptr;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] += p.scale * dqt[nb][4 * a4 + e];
+      *ptr = o4;
+    }
+}
+
+template <int D>
+hipError_t launch_d(const BwdParams& p, hipStream_t s) {
+  const int n_kt = (p.len_kv + 32 * kNW - 1) / (32 * kNW);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)(n_kt * p.heads_kv)), dim3(kNT), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_qt = (p.len_q + 32 * kNW - 1) / (32 * kNW);
+  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(n_qt * p.heads_q)), dim3(kNT), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s) {
+  if (p.head_dim == 128) return launch_d<128>(p, s);
+  if (p.head_dim == 64) return launch_d<64>(p, s);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace cpa

@@ -63,6 +63,48 @@ __device__ __forceinline__ int swz_rows(int j) {
 // Transposed tile (rows n, 8 chunks of 8 keys per row).
 __device__ __forceinline__ int swz_t(int n) { return (n & 7) ^ ((n >> 3) & 1); }
 
+// Row-major bf16 tile of D columns in LDS. Its 16-byte chunks are XOR-swizzled per row so that
+// both the row reads (8 consecutive columns of rows perm_row(l%32)) and the transposed reads
+// (one column of 4 consecutive rows per 16-lane group) spread over all banks.
+template <int D>
+__device__ __forceinline__ int tile_swz(int r) {
+  if constexpr (D >= 128) return ((r & 3) << 1) | ((r >> 3) & 1) | (((r >> 2) & 1) << 3);
+  else return ((r & 3) << 1) | ((r >> 3) & 1);
+}
+// Element offset of 16-byte chunk `chunk` (columns 8*chunk .. 8*chunk+7) of row r.
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int chunk) {
+  return r * D + 8 * (chunk ^ tile_swz<D>(r));
+}
+// Row operand: columns [8*chunk, 8*chunk + 8) of row r.
+template <int D>
+__device__ __forceinline__ u32x4_t tile_row8(const uint16_t* t, int r, int chunk) {
+  return *reinterpret_cast<const u32x4_t*>(t + tile_off<D>(r, chunk));
+}
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// Transposed operand of a row-major tile X via two ds_read_b64_tr_b16: lane l gets
+// X[r0 + 8*(l/32) + t][c0 + l%32] in slot t = 0..7, i.e. the MFMA operand of X^T for the 16
+// rows r0 .. r0+15 and 32 columns c0 .. c0+31 (r0 % 16 == 0, c0 % 32 == 0).
+// Each 16-lane group of ds_read_b64_tr_b16 transposes a 4-row x 16-column block: lane j
+// addresses row j/4, columns 4*(j%4) .. +3, and lane i receives column i of the block.
+template <int D>
+__device__ __forceinline__ u32x4_t tile_col8(const uint16_t* t, int r0, int c0, int lane) {
+  const int grp = lane >> 4, li = lane & 15;
+  const int col = c0 + 16 * (grp & 1) + 4 * (li & 3);
+  const int row = r0 + 8 * (grp >> 1) + (li >> 2);
+  const int chunk = col >> 3, sub = col & 7;
+  const uint16_t* a0 = t + tile_off<D>(row, chunk) + sub;
+  const uint16_t* a1 = t + tile_off<D>(row + 4, chunk) + sub;
+  const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a0));
+  const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a1));
+  const u32x2_t w0 = __builtin_bit_cast(u32x2_t, v0);
+  const u32x2_t w1 = __builtin_bit_cast(u32x2_t, v1);
+  return u32x4_t{w0[0], w0[1], w1[0], w1[1]};
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2). Map hardware
 // block ids so that consecutive work items land on the same XCD: XCD x runs items
 // [x * n/8, (x+1) * n/8). Bijective on [0, n).
