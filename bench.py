@@ -42,7 +42,9 @@ def parse():
                     help="step into scratch + cp_attn_merge instead of the fused fold")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the oracle CPU baseline (0 disables it)")
-    ap.add_argument("--merge-bench", action="store_true", default=True)
+    ap.add_argument("--no-merge-bench", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 1 GiB device copy first (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -81,6 +83,14 @@ def main():
     dk = torch.zeros(kc.shape, dtype=torch.float32, device=dev)
     dv = torch.zeros(kc.shape, dtype=torch.float32, device=dev)
 
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1.0)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
     sched = [(c, cls) for c, cls in cp.ring_schedule(wl.n_cp, rank, wl.causal)
              if cls != configs.SKIP]
 
@@ -106,7 +116,7 @@ def main():
                   file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
 
-    def run_step(ev_f=None, ev_b=None):
+    def run_step(ev_f=None, ev_b=None, ev_q=None):
         first = True
         for i, (c, _) in enumerate(sched):
             if ev_f is not None:
@@ -130,10 +140,16 @@ def main():
             for i, (c, _) in enumerate(sched):
                 if ev_b is not None:
                     ev_b[i][0].record(stream)
-                cp.bwd(q, kc[c], vc[c], d_o, lse, delta, dq, dk[c], dv[c], q_pos0=rank * lc,
-                       kv_pos0=c * lc, causal=wl.causal)
+                cp.bwd_dkdv(q, kc[c], vc[c], d_o, lse, delta, dk[c], dv[c], q_pos0=rank * lc,
+                            kv_pos0=c * lc, causal=wl.causal)
                 if ev_b is not None:
                     ev_b[i][1].record(stream)
+                if ev_q is not None:
+                    ev_q[i][0].record(stream)
+                cp.bwd_dq(q, kc[c], vc[c], d_o, lse, delta, dq, q_pos0=rank * lc,
+                          kv_pos0=c * lc, causal=wl.causal)
+                if ev_q is not None:
+                    ev_q[i][1].record(stream)
 
     for _ in range(args.warmup):
         run_step()
@@ -143,36 +159,45 @@ def main():
     mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     evs_f = [[(mk(), mk()) for _ in sched] for _ in range(args.steps)]
     evs_b = [[(mk(), mk()) for _ in sched] for _ in range(args.steps)]
+    evs_q = [[(mk(), mk()) for _ in sched] for _ in range(args.steps)]
     start, end = mk(), mk()
     torch.cuda.synchronize()
     start.record(stream)
     for s in range(args.steps):
-        run_step(evs_f[s], evs_b[s] if do_bwd else None)
+        run_step(evs_f[s], evs_b[s] if do_bwd else None, evs_q[s] if do_bwd else None)
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / args.steps
     fwd_ms = sum(a.elapsed_time(b) for st in evs_f for a, b in st) / args.steps
-    bwd_ms = (sum(a.elapsed_time(b) for st in evs_b for a, b in st) / args.steps) if do_bwd else 0.0
+    dkdv_ms = (sum(a.elapsed_time(b) for st in evs_b for a, b in st) / args.steps) if do_bwd else 0.0
+    dq_ms = (sum(a.elapsed_time(b) for st in evs_q for a, b in st) / args.steps) if do_bwd else 0.0
+    bwd_ms = dkdv_ms + dq_ms
     f_fwd = sum(fwd_step_flops)
     f_bwd = sum(bwd_step_flops) if do_bwd else 0.0
     print(f"# timed {args.steps} steps: {ms_step:.2f} ms/step (fwd kernels {fwd_ms:.2f} ms, "
-          f"bwd kernels {bwd_ms:.2f} ms)", file=sys.stderr, flush=True)
+          f"dK/dV kernels {dkdv_ms:.2f} ms, dQ kernels {dq_ms:.2f} ms)", file=sys.stderr,
+          flush=True)
 
-    # dominant kernel: the one with the larger share of the step
-    if do_bwd and bwd_ms > fwd_ms:
-        dom_name, dom_ms, dom_flops, n_launch = "cp_attn_bwd", bwd_ms, f_bwd, len(sched)
-    else:
-        dom_name, dom_ms, dom_flops, n_launch = "cp_attn_step (fwd_bf16_kernel)", fwd_ms, f_fwd, len(sched)
+    # Dominant kernel: the one with the largest share of the step. Algorithmic flops per launch:
+    # forward 4*d*H_q per visible pair (QK^T, PV); dK/dV kernel 8*d*H_q (S recompute, dP, dV,
+    # dK); dQ kernel 6*d*H_q (S, dP, dQ). Summed over the step's launches / summed durations.
+    cands = [("fwd_bf16_kernel (cp_attn_step)", fwd_ms, f_fwd)]
+    if do_bwd:
+        cands.append(("bwd_dkdv_kernel (cp_attn_bwd_dkdv)", dkdv_ms, f_bwd * 0.8))
+        cands.append(("bwd_dq_kernel (cp_attn_bwd_dq)", dq_ms, f_bwd * 0.6))
+    dom_name, dom_ms, dom_flops = max(cands, key=lambda c: c[1])
+    n_launch = len(sched)
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    traffic = measured_traffic(wl.name, dom_name.split(" ")[0])
     roofline = {"bound": "mfma", "kernel": dom_name, "achieved": round(achieved, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "launches_per_step": n_launch,
                 "avg_launch_ms": round(dom_ms / n_launch, 4)}
 
     merge_info = None
-    if args.merge_bench:
+    if not args.no_merge_bench:
         merge_info = bench_merge(cp, torch, o, lse)
 
     cpu = None
@@ -200,6 +225,8 @@ def main():
         "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
         "fwd_frac_of_peak": round(f_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2) if do_bwd else None,
+        "kernel_ms_per_step": {"fwd": round(fwd_ms, 3), "bwd_dkdv": round(dkdv_ms, 3),
+                               "bwd_dq": round(dq_ms, 3)},
         "bwd_frac_of_peak": (round(f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
                              if do_bwd else None),
         "tokens_per_s": round(lc / (ms_step * 1e-3), 1),
@@ -208,6 +235,35 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+KERNEL_SOURCES = {"fwd_bf16_kernel": "fwd_bf16.hip", "bwd_dkdv_kernel": "bwd_bf16.hip",
+                  "bwd_dq_kernel": "bwd_bf16.hip", "merge_kernel": "elementwise.hip",
+                  "prep_kernel": "elementwise.hip"}
+
+
+def measured_traffic(workload_name, kernel):
+    """HBM bytes per launch (read + written) of `kernel` from the committed rocprofv3 counter
+    summary of this workload (FETCH_SIZE / WRITE_SIZE scaled by a 1 GiB copy), or None when no
+    summary exists or the kernel's source changed since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"{workload_name}_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get("kernels", {}).get(kernel)
+    if rec is None or kernel not in KERNEL_SOURCES:
+        return None
+    h = hashlib.sha1()
+    csrc = os.path.join(ROOT, "long_context_sequence_amd", "csrc")
+    for name in (KERNEL_SOURCES[kernel], "device_common.hpp", "kernels.hpp"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != rec["source_sha1"]:
+        return None
+    return {"read_bytes": int(rec["read_bytes"]), "write_bytes": int(rec["write_bytes"]),
+            "total_bytes": int(rec["read_bytes"] + rec["write_bytes"])}
 
 
 def bench_merge(cp, torch, o, lse):

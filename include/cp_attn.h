@@ -128,6 +128,18 @@ cp_status cp_attn_bwd(const cp_attn_desc* desc, const void* q, const void* k, co
                       const void* d_o, const float* lse, const float* delta, float* dq,
                       float* dk, float* dv, void* stream);
 
+/*
+ * cp_attn_bwd_dkdv / cp_attn_bwd_dq — the two halves of cp_attn_bwd, one kernel each, same
+ * arguments and semantics: the first accumulates dk and dv only (dq is not touched and may be
+ * NULL), the second accumulates dq only (dk, dv may be NULL). cp_attn_bwd = both, in this order.
+ */
+cp_status cp_attn_bwd_dkdv(const cp_attn_desc* desc, const void* q, const void* k,
+                           const void* v, const void* d_o, const float* lse,
+                           const float* delta, float* dk, float* dv, void* stream);
+cp_status cp_attn_bwd_dq(const cp_attn_desc* desc, const void* q, const void* k, const void* v,
+                         const void* d_o, const float* lse, const float* delta, float* dq,
+                         void* stream);
+
 /* A whole rank's ring, run natively: the schedule below with one cp_attn_step per visited
  * chunk (accumulating, or step + cp_attn_merge when o_work/lse_work are given). */
 typedef struct {

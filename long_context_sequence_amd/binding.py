@@ -68,6 +68,10 @@ def load():
     lib.cp_attn_bwd_prep.restype = st
     lib.cp_attn_bwd.argtypes = [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.cp_attn_bwd.restype = st
+    lib.cp_attn_bwd_dkdv.argtypes = [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.cp_attn_bwd_dkdv.restype = st
+    lib.cp_attn_bwd_dq.argtypes = [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.cp_attn_bwd_dq.restype = st
     lib.cp_ring_schedule.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
     lib.cp_ring_schedule.restype = ctypes.c_int32
@@ -167,14 +171,18 @@ def bwd_prep(o, d_o, delta):
                   allow_skip=False)
 
 
-def bwd(q, k, v, d_o, lse, delta, dq, dk, dv, q_pos0=0, kv_pos0=0, causal=False, scale=None):
-    """cp_attn_bwd: dq, dk, dv (fp32) are accumulated."""
+def _bwd_inputs(q, k, v, d_o, lse, delta):
     _need(q, "q")
     _need(k, "k", dtype=q.dtype)
     _need(v, "v", shape=k.shape, dtype=q.dtype)
     _need(d_o, "d_o", shape=q.shape, dtype=q.dtype)
     _need(lse, "lse", shape=q.shape[:2], dtype=torch.float32)
     _need(delta, "delta", shape=q.shape[:2], dtype=torch.float32)
+
+
+def bwd(q, k, v, d_o, lse, delta, dq, dk, dv, q_pos0=0, kv_pos0=0, causal=False, scale=None):
+    """cp_attn_bwd: dq, dk, dv (fp32) are accumulated."""
+    _bwd_inputs(q, k, v, d_o, lse, delta)
     _need(dq, "dq", shape=q.shape, dtype=torch.float32)
     _need(dk, "dk", shape=k.shape, dtype=torch.float32)
     _need(dv, "dv", shape=k.shape, dtype=torch.float32)
@@ -182,6 +190,27 @@ def bwd(q, k, v, d_o, lse, delta, dq, dk, dv, q_pos0=0, kv_pos0=0, causal=False,
     return _check(load().cp_attn_bwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(d_o),
                                      _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv),
                                      _stream()), "cp_attn_bwd")
+
+
+def bwd_dkdv(q, k, v, d_o, lse, delta, dk, dv, q_pos0=0, kv_pos0=0, causal=False, scale=None):
+    """cp_attn_bwd_dkdv: the dK/dV half of cp_attn_bwd (dk, dv accumulated)."""
+    _bwd_inputs(q, k, v, d_o, lse, delta)
+    _need(dk, "dk", shape=k.shape, dtype=torch.float32)
+    _need(dv, "dv", shape=k.shape, dtype=torch.float32)
+    d = _desc(q, k, q_pos0, kv_pos0, causal, scale, False)
+    return _check(load().cp_attn_bwd_dkdv(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(d_o),
+                                          _ptr(lse), _ptr(delta), _ptr(dk), _ptr(dv), _stream()),
+                  "cp_attn_bwd_dkdv")
+
+
+def bwd_dq(q, k, v, d_o, lse, delta, dq, q_pos0=0, kv_pos0=0, causal=False, scale=None):
+    """cp_attn_bwd_dq: the dQ half of cp_attn_bwd (dq accumulated)."""
+    _bwd_inputs(q, k, v, d_o, lse, delta)
+    _need(dq, "dq", shape=q.shape, dtype=torch.float32)
+    d = _desc(q, k, q_pos0, kv_pos0, causal, scale, False)
+    return _check(load().cp_attn_bwd_dq(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(d_o),
+                                        _ptr(lse), _ptr(delta), _ptr(dq), _stream()),
+                  "cp_attn_bwd_dq")
 
 
 def ring_schedule(n_cp: int, rank: int, causal: bool):

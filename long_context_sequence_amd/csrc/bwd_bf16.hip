@@ -338,21 +338,27 @@ __global__ void __launch_bounds__(kNT, 1) bwd_dq_kernel(BwdParams p) {
 }
 
 template <int D>
-hipError_t launch_d(const BwdParams& p, hipStream_t s) {
-  const int n_kt = (p.len_kv + 32 * kNW - 1) / (32 * kNW);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)(n_kt * p.heads_kv)), dim3(kNT), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int n_qt = (p.len_q + 32 * kNW - 1) / (32 * kNW);
-  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(n_qt * p.heads_q)), dim3(kNT), 0, s, p);
-  return hipGetLastError();
+hipError_t launch_d(const BwdParams& p, int which, hipStream_t s) {
+  if (which & 1) {
+    const int n_kt = (p.len_kv + 32 * kNW - 1) / (32 * kNW);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)(n_kt * p.heads_kv)), dim3(kNT), 0,
+                       s, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (which & 2) {
+    const int n_qt = (p.len_q + 32 * kNW - 1) / (32 * kNW);
+    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(n_qt * p.heads_q)), dim3(kNT), 0, s, p);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s) {
-  if (p.head_dim == 128) return launch_d<128>(p, s);
-  if (p.head_dim == 64) return launch_d<64>(p, s);
+hipError_t launch_bwd_bf16(const BwdParams& p, int which, hipStream_t s) {
+  if (p.head_dim == 128) return launch_d<128>(p, which, s);
+  if (p.head_dim == 64) return launch_d<64>(p, which, s);
   return hipErrorInvalidValue;
 }
 

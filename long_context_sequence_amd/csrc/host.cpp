@@ -166,16 +166,29 @@ cp_status cp_attn_bwd_prep(int64_t rows, int32_t head_dim, int32_t dtype, const 
                                        static_cast<hipStream_t>(stream)));
 }
 
-cp_status cp_attn_bwd(const cp_attn_desc* desc, const void* q, const void* k, const void* v,
-                      const void* d_o, const float* lse, const float* delta, float* dq,
-                      float* dk, float* dv, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of the backward entry points. which: 1 = dK/dV, 2 = dQ, 3 = both.
+cp_status bwd_impl(const cp_attn_desc* desc, const void* q, const void* k, const void* v,
+                   const void* d_o, const float* lse, const float* delta, float* dq, float* dk,
+                   float* dv, int which, void* stream) {
   cp_status st = check_desc(desc);
   if (st != CP_OK) return st;
   if (desc->dtype != CP_BF16) return CP_ERR_UNSUPPORTED;
   if (desc->len_q == 0 || desc->len_kv == 0) return CP_OK;
   if (causally_empty(desc)) return CP_STEP_SKIPPED;
-  st = check_ptrs({q, k, v, d_o, lse, delta, dq, dk, dv});
+  st = check_ptrs({q, k, v, d_o, lse, delta});
   if (st != CP_OK) return st;
+  if (which & 1) {
+    st = check_ptrs({dk, dv});
+    if (st != CP_OK) return st;
+  }
+  if (which & 2) {
+    st = check_ptrs({dq});
+    if (st != CP_OK) return st;
+  }
   cpa::BwdParams p;
   p.q = q;
   p.k = k;
@@ -197,7 +210,29 @@ cp_status cp_attn_bwd(const cp_attn_desc* desc, const void* q, const void* k, co
   p.causal = desc->causal;
   p.scale = resolve_scale(desc);
   p.scale_log2 = p.scale * 1.4426950408889634f;
-  return from_hip(cpa::launch_bwd_bf16(p, static_cast<hipStream_t>(stream)));
+  return from_hip(cpa::launch_bwd_bf16(p, which, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+cp_status cp_attn_bwd(const cp_attn_desc* desc, const void* q, const void* k, const void* v,
+                      const void* d_o, const float* lse, const float* delta, float* dq,
+                      float* dk, float* dv, void* stream) {
+  return bwd_impl(desc, q, k, v, d_o, lse, delta, dq, dk, dv, 3, stream);
+}
+
+cp_status cp_attn_bwd_dkdv(const cp_attn_desc* desc, const void* q, const void* k,
+                           const void* v, const void* d_o, const float* lse,
+                           const float* delta, float* dk, float* dv, void* stream) {
+  return bwd_impl(desc, q, k, v, d_o, lse, delta, nullptr, dk, dv, 1, stream);
+}
+
+cp_status cp_attn_bwd_dq(const cp_attn_desc* desc, const void* q, const void* k, const void* v,
+                         const void* d_o, const float* lse, const float* delta, float* dq,
+                         void* stream) {
+  return bwd_impl(desc, q, k, v, d_o, lse, delta, dq, nullptr, nullptr, 2, stream);
 }
 
 int32_t cp_ring_schedule(int32_t n_cp, int32_t rank, int32_t causal, int32_t* chunks,

@@ -46,6 +46,7 @@ hipError_t launch_merge(long long rows, int head_dim, float* o_acc, float* lse_a
                         const float* o, const float* lse, hipStream_t s);
 hipError_t launch_bwd_prep(long long rows, int head_dim, int is_bf16, const float* o,
                            const void* d_o, float* delta, hipStream_t s);
-hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s);
+// which: 1 = dK/dV kernel, 2 = dQ kernel, 3 = both.
+hipError_t launch_bwd_bf16(const BwdParams& p, int which, hipStream_t s);
 
 }  // namespace cpa
