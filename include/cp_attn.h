@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define CP_MAX_LEN (1 << 24)
+#define CP_MAX_LEN (1 << 23)   /* rows per shard/chunk: keeps per-head byte offsets < 4 GB */
 #define CP_MAX_HEADS 1024
 
 typedef enum {

@@ -25,35 +25,6 @@ constexpr int kKT = 64;    // keys per tile (dq)
 constexpr int kNW = 4;     // waves per workgroup
 constexpr int kNT = 64 * kNW;
 
-// Stage a rows x D bf16 tile (rows from `row0`, zero past `nrows`) into registers; then LDS.
-template <int D, int ROWS>
-struct TileStager {
-  static constexpr int CH = D / 8;
-  static constexpr int LD = ROWS * CH / kNT;
-  static_assert(ROWS * CH % kNT == 0, "tile must split evenly over the threads");
-  u32x4_t r[LD];
-  __device__ __forceinline__ void load(const uint16_t* src, int row0, int nrows, int tid) {
-#pragma unroll
-    for (int u = 0; u < LD; ++u) {
-      const int idx = tid + u * kNT;
-      const int rr = idx / CH, c = idx % CH;
-      const int row = row0 + rr;
-      const bool ok = row < nrows;
-      const int rc = ok ? row : nrows - 1;
-      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(src + (size_t)rc * D + 8 * c);
-      r[u] = ok ? x : u32x4_t{0u, 0u, 0u, 0u};
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* dst, int tid) const {
-#pragma unroll
-    for (int u = 0; u < LD; ++u) {
-      const int idx = tid + u * kNT;
-      const int rr = idx / CH, c = idx % CH;
-      *reinterpret_cast<u32x4_t*>(dst + tile_off<D>(rr, c)) = r[u];
-    }
-  }
-};
-
 template <int D>
 __global__ void __launch_bounds__(kNT, 1) bwd_dkdv_kernel(BwdParams p) {
   constexpr int KS = D / 16, NB = D / 32, BNK = 32 * kNW;
@@ -102,7 +73,7 @@ __global__ void __launch_bounds__(kNT, 1) bwd_dkdv_kernel(BwdParams p) {
     dvt[nb] = f32x16_t{};
   }
 
-  TileStager<D, kQT> stq, stdo;
+  TileStager<D, kQT, kNT> stq, stdo;
   float st_lse = 0.f, st_del = 0.f;
   auto load_it = [&](int it) {
     const int h = g * p.group + it / per_head;
@@ -136,19 +107,20 @@ __global__ void __launch_bounds__(kNT, 1) bwd_dkdv_kernel(BwdParams p) {
   __syncthreads();
 
   const float c2 = p.scale_log2;
-  const long long key_pos = p.kv_pos0 + key;                    // this lane's key position
-  const long long wave_k0 = p.kv_pos0 + kv_base + 32 * wave;   // first key position of the wave
+  const int dpos = causal_shift(p.q_pos0, p.kv_pos0);
+  const int wave_key0 = kv_base + 32 * wave;  // first key of the wave
 
   for (int it = 0; it < n_it; ++it) {
     const int buf = it & 1;
     if (it + 1 < n_it) load_it(it + 1);
     const int q0 = (qt_first + it % per_head) * kQT;
-    const long long qpos0 = p.q_pos0 + q0;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const long long bpos = qpos0 + 32 * b;  // position of the block's first row
-      if (p.causal && bpos + 31 < wave_k0) continue;  // no row of the block sees the wave's keys
-      const bool need_mask = p.causal && bpos < wave_k0 + 31;
+      const int brow = q0 + 32 * b;  // first row of the block
+      // no row of the block sees the wave's first key: nothing to do
+      if (p.causal && wave_key0 - (brow + 31) > dpos) continue;
+      // some key of the wave invisible to the block's first row: mask
+      const bool need_mask = p.causal && wave_key0 + 31 - brow > dpos;
       f32x16_t s = f32x16_t{}, dp = f32x16_t{};
       const int arow = 32 * b + perm_row(col);
 #pragma unroll
@@ -168,7 +140,7 @@ __global__ void __launch_bounds__(kNT, 1) bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * a4 + e], c2, -l4[e]));
-          if (need_mask && key_pos > qpos0 + rbase + e) pr = 0.f;
+          if (need_mask && key - (q0 + rbase + e) > dpos) pr = 0.f;
           pv[e] = pr;
           dsv[e] = pr * (dp[4 * a4 + e] - d4[e]);
         }
@@ -254,7 +226,7 @@ __global__ void __launch_bounds__(kNT, 1) bwd_dq_kernel(BwdParams p) {
 
   const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (size_t)g * p.len_kv * D;
   const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (size_t)g * p.len_kv * D;
-  TileStager<D, kKT> stk, stv;
+  TileStager<D, kKT, kNT> stk, stv;
 
   f32x16_t dqt[NB];
 #pragma unroll
@@ -269,8 +241,8 @@ __global__ void __launch_bounds__(kNT, 1) bwd_dq_kernel(BwdParams p) {
   __syncthreads();
 
   const float c2 = p.scale_log2;
-  const long long wave_q0 = p.q_pos0 + q_base + 32 * wave;
-  const long long qpos = wave_q0 + col;
+  const int dpos = causal_shift(p.q_pos0, p.kv_pos0);
+  const int wave_row0 = q_base + 32 * wave;
 
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt & 1;
@@ -278,11 +250,11 @@ __global__ void __launch_bounds__(kNT, 1) bwd_dq_kernel(BwdParams p) {
       stk.load(kg, (kt + 1) * kKT, p.len_kv, tid);
       stv.load(vg, (kt + 1) * kKT, p.len_kv, tid);
     }
-    const long long key_pos0 = p.kv_pos0 + (long long)kt * kKT;
-    const bool wave_visible = !p.causal || key_pos0 <= wave_q0 + 31;
+    const int key0 = kt * kKT;
+    const bool wave_visible = !p.causal || key0 - (wave_row0 + 31) <= dpos;
     if (wave_visible) {
       const bool need_mask =
-          (kt * kKT + kKT > p.len_kv) || (p.causal && key_pos0 + kKT - 1 > wave_q0);
+          key0 + kKT > p.len_kv || (p.causal && key0 + kKT - 1 - wave_row0 > dpos);
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
         f32x16_t s = f32x16_t{}, dp = f32x16_t{};
@@ -302,8 +274,9 @@ __global__ void __launch_bounds__(kNT, 1) bwd_dq_kernel(BwdParams p) {
             const int r = 2 * r2 + e;
             float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -lse2));
             if (need_mask) {
-              const int kk = kt * kKT + 32 * blk + perm_row(8 * (r >> 2) + 4 * half + (r & 3));
-              if (kk >= p.len_kv || (p.causal && p.kv_pos0 + kk > qpos)) pr = 0.f;
+              const int kk = key0 + 32 * blk + perm_row(8 * (r >> 2) + 4 * half + (r & 3));
+              const bool vis = (kk < p.len_kv) & ((!p.causal) | (kk - qi <= dpos));
+              pr = vis ? pr : 0.f;
             }
             dsv[e] = pr * (dp[r] - del);
           }

@@ -53,23 +53,17 @@ __device__ __forceinline__ int perm_row(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
-// 16-byte-chunk swizzles that keep the MFMA operand reads of the LDS tiles bank-conflict free.
-// Row-major tile of rows j with C chunks per row (C = 16 for d = 128, 8 for d = 64).
-template <int C>
-__device__ __forceinline__ int swz_rows(int j) {
-  if constexpr (C >= 16) return (j & 3) | ((j & 8) >> 1) | ((j & 4) << 1);
-  else return (j & 3) | ((j & 8) >> 1);
-}
-// Transposed tile (rows n, 8 chunks of 8 keys per row).
-__device__ __forceinline__ int swz_t(int n) { return (n & 7) ^ ((n >> 3) & 1); }
-
-// Row-major bf16 tile of D columns in LDS. Its 16-byte chunks are XOR-swizzled per row so that
-// both the row reads (8 consecutive columns of rows perm_row(l%32)) and the transposed reads
-// (one column of 4 consecutive rows per 16-lane group) spread over all banks.
+// Row-major bf16 tile of D columns in LDS (64 banks of 4 bytes: a ds_read_b128 serves 16 lanes
+// per pass, a ds_read_b64 32 lanes). Its 16-byte chunks are XOR-swizzled per row:
+//  * bits 2-3 of the swizzle = row % 4, so the 4 consecutive rows a transpose read touches land
+//    in 4 different 64-byte quarters of the 256-byte bank window;
+//  * bits 0-1 = rows bits 3 and 2, so the 16 rows perm_row(0..15) of a row read land on 16
+//    different chunk positions.
+// (For d = 64 a row is half the bank window, so row bit 1 takes the place of row % 4.)
 template <int D>
 __device__ __forceinline__ int tile_swz(int r) {
-  if constexpr (D >= 128) return ((r & 3) << 1) | ((r >> 3) & 1) | (((r >> 2) & 1) << 3);
-  else return ((r & 3) << 1) | ((r >> 3) & 1);
+  if constexpr (D >= 128) return ((r & 3) << 2) | ((r >> 3) & 1) | (((r >> 2) & 1) << 1);
+  else return (((r >> 1) & 1) << 2) | ((r >> 3) & 1) | (((r >> 2) & 1) << 1);
 }
 // Element offset of 16-byte chunk `chunk` (columns 8*chunk .. 8*chunk+7) of row r.
 template <int D>
@@ -103,6 +97,77 @@ __device__ __forceinline__ u32x4_t tile_col8(const uint16_t* t, int r0, int c0, 
   const u32x2_t w0 = __builtin_bit_cast(u32x2_t, v0);
   const u32x2_t w1 = __builtin_bit_cast(u32x2_t, v1);
   return u32x4_t{w0[0], w0[1], w1[0], w1[1]};
+}
+
+// Copies a ROWS x D bf16 tile (rows row0.. of a row-major [nrows, D] array, zero past nrows)
+// from global memory into registers (load) and then into a swizzled LDS tile (store), with
+// NT threads; 16 consecutive lanes cover one 256-byte row, so the global loads are coalesced.
+template <int D, int ROWS, int NT>
+struct TileStager {
+  static constexpr int CH = D / 8;
+  static constexpr int LD = ROWS * CH / NT;
+  static_assert(ROWS * CH % NT == 0, "tile must split evenly over the threads");
+  u32x4_t r[LD];
+  __device__ __forceinline__ void load(const uint16_t* src, int row0, int nrows, int tid) {
+#pragma unroll
+    for (int u = 0; u < LD; ++u) {
+      const int idx = tid + u * NT;
+      const int rr = idx / CH, c = idx % CH;
+      const int row = row0 + rr;
+      const bool ok = row < nrows;
+      const int rc = ok ? row : nrows - 1;
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(src + (size_t)rc * D + 8 * c);
+      r[u] = ok ? x : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* dst, int tid) const {
+#pragma unroll
+    for (int u = 0; u < LD; ++u) {
+      const int idx = tid + u * NT;
+      const int rr = idx / CH, c = idx % CH;
+      *reinterpret_cast<u32x4_t*>(dst + tile_off<D>(rr, c)) = r[u];
+    }
+  }
+};
+
+// Buffer resource over `bytes` bytes at `base`: loads past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Direct global -> LDS copy of a ROWS x D bf16 tile into the swizzled layout (no registers, no
+// LDS store instructions). One buffer_load_dwordx4 ... lds per wave fills 1 KB of LDS at
+// consecutive 16-byte slots, i.e. 1024 / (2D) whole rows; each lane fetches the source chunk that
+// belongs at its slot. Rows past the end of the buffer read as zeros. Completion is tracked by
+// vmcnt: wait for it before the barrier that publishes the tile.
+template <int D, int ROWS, int NT>
+struct TileDma {
+  static constexpr int CH = D / 8;                 // 16-byte chunks per row
+  static constexpr int RPI = 64 / CH;              // rows per wave instruction
+  static constexpr int NWAVE = NT / 64;
+  static constexpr int ITERS = ROWS / (RPI * NWAVE);
+  static_assert(ROWS % (RPI * NWAVE) == 0, "tile must split evenly over the waves");
+  __device__ __forceinline__ static void issue(__amdgpu_buffer_rsrc_t rsrc, int row0,
+                                               uint16_t* lds_tile, int wave, int lane) {
+#pragma unroll
+    for (int u = 0; u < ITERS; ++u) {
+      const int rbase = (u * NWAVE + wave) * RPI;
+      const int r = rbase + lane / CH;
+      const int c = (lane % CH) ^ tile_swz<D>(r);
+      const unsigned voff = ((unsigned)(row0 + r) * D + 8u * c) * 2u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)(lds_tile + rbase * D), 16, voff, 0, 0, 0);
+    }
+  }
+};
+
+// Causal visibility in chunk-local coordinates: key j is visible to query i iff
+// kv_pos0 + j <= q_pos0 + i, i.e. j - i <= q_pos0 - kv_pos0. The difference is clamped to a
+// range where the 32-bit test stays exact for local indices below 2^24.
+__device__ __forceinline__ int causal_shift(long long q_pos0, long long kv_pos0) {
+  const long long d = q_pos0 - kv_pos0;
+  return (int)(d > (1ll << 30) ? (1ll << 30) : (d < -(1ll << 30) ? -(1ll << 30) : d));
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2). Map hardware

@@ -4,7 +4,7 @@
 //
 // Work decomposition
 //   workgroup = NW waves = one query head x BM = 32*NW query rows; each wave owns 32 rows.
-//   Keys stream through LDS in tiles of 64 (double buffered): K row-major, V transposed.
+//   Keys stream through LDS in tiles of 64 (double buffered), K and V both row-major.
 //
 // Register-level formulation (per wave, per 64-key tile)
 //   S^T[key][query] = K Q^T      A = K rows from LDS, B = the wave's Q rows held in registers
@@ -14,7 +14,8 @@
 // With S^T, each lane's accumulator column is one query row, so the row max needs one swap with
 // the lane 32 apart, the row sum stays lane-local until the end and the O rescale is one scalar
 // per lane. Loading K row perm_row(m) for MFMA row m makes every run of 8 accumulator registers
-// cover 8 consecutive keys, so the matching V^T operand is one 16-byte LDS read.
+// cover 8 consecutive keys, so the matching V^T operand is one transpose read (two
+// ds_read_b64_tr_b16) of the row-major V tile.
 //
 // Causality: a tile is computed only if some key in it is visible to some row of the wave;
 // the mask is applied only on tiles that straddle the diagonal or the ragged end of the chunk.
@@ -26,27 +27,15 @@
 namespace cpa {
 namespace {
 
-constexpr int kBN = 64;  // keys per tile
-
-template <int D, int NW>
-struct FwdShape {
-  static constexpr int NT = NW * 64;            // threads
-  static constexpr int BM = 32 * NW;            // query rows per workgroup
-  static constexpr int KCH = D / 8;             // 16-byte chunks per K row
-  static constexpr int KS = D / 16;             // k-steps of Q K^T
-  static constexpr int NB = D / 32;             // 32-row blocks of O^T
-  static constexpr int KLD = kBN * KCH / NT;    // K chunks staged per thread
-  static constexpr int VUNITS = (kBN / 8) * (D / 4);  // V pieces of 8 keys x 4 columns
-  static constexpr int VLD = (VUNITS + NT - 1) / NT;
-  static_assert(kBN * KCH % NT == 0, "K tile must split evenly over the threads");
-};
+constexpr int kBN = 64;       // keys per tile
+constexpr float kTau = 8.f;   // the reference max moves only when a row max grows by more than
+                              // this (log2 units): P stays <= 2^8 and most tiles skip the rescale
 
 template <int D, int NW>
 __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(StepParams p) {
-  using S = FwdShape<D, NW>;
-  constexpr int NT = S::NT, BM = S::BM, KCH = S::KCH, KS = S::KS, NB = S::NB;
+  constexpr int NT = NW * 64, BM = 32 * NW, KS = D / 16, NB = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t sk[2][kBN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t svt[2][D * kBN];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[2][kBN * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
@@ -83,113 +72,57 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(StepParams p) {
   long long nk = p.len_kv;
   if (p.causal) nk = min(nk, p.q_pos0 + last_row - p.kv_pos0 + 1);
   const int n_kt = nk > 0 ? (int)((nk + kBN - 1) / kBN) : 0;
+  const int dpos = causal_shift(p.q_pos0, p.kv_pos0);
+  const int wave_row0 = q_base + 32 * wave;
 
-  u32x4_t kst[S::KLD];
-  u32x2_t vst[S::VLD][8];
-
-  auto load_tile = [&](int kt) {
-    const int key0 = kt * kBN;
-#pragma unroll
-    for (int u = 0; u < S::KLD; ++u) {
-      const int idx = tid + u * NT;
-      const int r = idx / KCH, c = idx % KCH;
-      const int key = key0 + r;
-      const bool ok = key < p.len_kv;
-      const int kc = ok ? key : p.len_kv - 1;
-      u32x4_t x = *reinterpret_cast<const u32x4_t*>(kg + (size_t)kc * D + 8 * c);
-      kst[u] = ok ? x : u32x4_t{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < S::VLD; ++u) {
-      const int unit = tid + u * NT;
-      if (unit < S::VUNITS) {
-        const int cg = unit % (D / 4), rg = unit / (D / 4);
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int key = key0 + 8 * rg + r;
-          const bool ok = key < p.len_kv;
-          const int kc = ok ? key : p.len_kv - 1;
-          u32x2_t x = *reinterpret_cast<const u32x2_t*>(vg + (size_t)kc * D + 4 * cg);
-          vst[u][r] = ok ? x : u32x2_t{0u, 0u};
-        }
-      }
-    }
-  };
-
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < S::KLD; ++u) {
-      const int idx = tid + u * NT;
-      const int r = idx / KCH, c = idx % KCH;
-      const int pos = c ^ swz_rows<KCH>(r);
-      *reinterpret_cast<u32x4_t*>(&sk[buf][r * D + 8 * pos]) = kst[u];
-    }
-#pragma unroll
-    for (int u = 0; u < S::VLD; ++u) {
-      const int unit = tid + u * NT;
-      if (unit < S::VUNITS) {
-        const int cg = unit % (D / 4), rg = unit / (D / 4);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          // column n = 4*cg + c of keys 8*rg .. 8*rg+7, packed two keys per word
-          const int n = 4 * cg + c;
-          const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-          u32x4_t out;
-#pragma unroll
-          for (int pq = 0; pq < 4; ++pq)
-            out[pq] = __builtin_amdgcn_perm(vst[u][2 * pq + 1][c >> 1], vst[u][2 * pq][c >> 1], sel);
-          const int pos = rg ^ swz_t(n);
-          *reinterpret_cast<u32x4_t*>(&svt[buf][n * kBN + 8 * pos]) = out;
-        }
-      }
-    }
-  };
+  using Dma = TileDma<D, kBN, NT>;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg, (unsigned)p.len_kv * D * 2u);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg, (unsigned)p.len_kv * D * 2u);
 
   f32x16_t oacc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x16_t{};
-  float m_run = -INFINITY;  // running row max of scale*log2(e)*s
+  float m_run = -INFINITY;  // reference row max of scale*log2(e)*s
   float l_run = 0.f;        // this lane's share of the running row sum
 
   if (n_kt > 0) {
-    load_tile(0);
-    store_tile(0);
+    Dma::issue(rk, 0, sk[0], wave, lane);
+    Dma::issue(rv, 0, sv[0], wave, lane);
   }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  const long long wave_q0 = p.q_pos0 + q_base + 32 * wave;  // global position of the wave's row 0
   const float c2 = p.scale_log2;
 
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < n_kt) load_tile(kt + 1);
-    const long long key_pos0 = p.kv_pos0 + (long long)kt * kBN;
-    const bool wave_visible = !p.causal || key_pos0 <= wave_q0 + 31;
+    if (kt + 1 < n_kt) {
+      Dma::issue(rk, (kt + 1) * kBN, sk[buf ^ 1], wave, lane);
+      Dma::issue(rv, (kt + 1) * kBN, sv[buf ^ 1], wave, lane);
+    }
+    const int key0 = kt * kBN;
+    // some key of the tile visible to the wave's last row?
+    const bool wave_visible = !p.causal || key0 - (wave_row0 + 31) <= dpos;
     if (wave_visible) {
       f32x16_t s[2];
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
         s[blk] = f32x16_t{};
         const int row = 32 * blk + perm_row(col);
-        const int sw = swz_rows<KCH>(row);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int pos = (2 * ks + half) ^ sw;
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&sk[buf][row * D + 8 * pos]);
-          s[blk] = mfma32x32x16(a, qreg[ks], s[blk]);
-        }
+        for (int ks = 0; ks < KS; ++ks)
+          s[blk] = mfma32x32x16(tile_row8<D>(sk[buf], row, 2 * ks + half), qreg[ks], s[blk]);
       }
-      const bool need_mask =
-          (kt * kBN + kBN > p.len_kv) || (p.causal && key_pos0 + kBN - 1 > wave_q0);
-      if (need_mask) {
-        const long long qpos = wave_q0 + col;
+      // every key of the tile visible to the wave's first row and inside the chunk?
+      const bool full = key0 + kBN <= p.len_kv && (!p.causal || key0 + kBN - 1 - wave_row0 <= dpos);
+      if (!full) {
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = kt * kBN + 32 * blk + perm_row(8 * (r >> 2) + 4 * half + (r & 3));
-            const bool vis = key < p.len_kv && (!p.causal || p.kv_pos0 + key <= qpos);
-            if (!vis) s[blk][r] = -INFINITY;
+            const int key = key0 + 32 * blk + perm_row(8 * (r >> 2) + 4 * half + (r & 3));
+            const bool vis = (key < p.len_kv) & ((!p.causal) | (key - qi <= dpos));
+            s[blk][r] = vis ? s[blk][r] : -INFINITY;
           }
       }
       float mx = -INFINITY;
@@ -197,12 +130,15 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(StepParams p) {
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[blk][r]);
-      mx = pair_max(mx);
-      const float m_new = fmaxf(m_run, mx * c2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
+      mx = pair_max(mx) * c2;
+      // Move the reference max only when the row max outgrew it by more than kTau (the first
+      // visible tile always does: m_run starts at -inf). P = exp2(s*c2 - m_run) <= 2^kTau.
+      const bool grow = mx > m_run + kTau;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
+      m_run = grow ? mx : m_run;
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
+      // P in bf16 as the PV operand; the row sum (and so the LSE) from the fp32 values.
       u32x4_t pb[4];
       float lsum = 0.f;
 #pragma unroll
@@ -213,29 +149,25 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(StepParams p) {
           for (int t = 0; t < 4; ++t) {
             const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][8 * q + 2 * t], c2, -m_use));
             const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][8 * q + 2 * t + 1], c2, -m_use));
-            lsum += p0 + p1;
             pb[2 * blk + q][t] = pack_bf16x2(p0, p1);
+            lsum += p0 + p1;
           }
       l_run = l_run * alpha + lsum;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[nb][r] *= alpha;
       }
+      // O^T += V^T P^T: the V^T operand for keys 16*kk .. 16*kk+15 via the transpose read.
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int n = 32 * nb + col;
-        const int sw = swz_t(n);
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int pos = (2 * kk + half) ^ sw;
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&svt[buf][n * kBN + 8 * pos]);
-          oacc[nb] = mfma32x32x16(a, pb[kk], oacc[nb]);
-        }
-      }
+        for (int kk = 0; kk < 4; ++kk)
+          oacc[nb] = mfma32x32x16(tile_col8<D>(sv[buf], 16 * kk, 32 * nb, lane), pb[kk], oacc[nb]);
     }
-    if (kt + 1 < n_kt) store_tile(buf ^ 1);
+    // the next tile's direct loads have landed, and every wave is done with this one
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 

@@ -69,7 +69,7 @@ def _step(d, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE):
     (dict(heads_q=3, heads_kv=2), CP_ERR_SHAPE),
     (dict(heads_q=0), CP_ERR_SHAPE),
     (dict(len_q=-1), CP_ERR_SHAPE),
-    (dict(len_kv=(1 << 24) + 1), CP_ERR_SHAPE),
+    (dict(len_kv=(1 << 23) + 1), CP_ERR_SHAPE),
     (dict(head_dim=96), CP_ERR_UNSUPPORTED),
     (dict(head_dim=0), CP_ERR_SHAPE),
     (dict(causal=2), CP_ERR_SHAPE),
