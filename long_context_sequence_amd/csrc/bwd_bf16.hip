@@ -73,15 +73,17 @@ __global__ void __launch_bounds__(kNT, 1) bwd_dkdv_kernel(BwdParams p) {
     dvt[nb] = f32x16_t{};
   }
 
-  TileStager<D, kQT, kNT> stq, stdo;
+  using Dma = TileDma<D, kQT, kNT>;
   float st_lse = 0.f, st_del = 0.f;
-  auto load_it = [&](int it) {
+  // Issue the direct loads of tile `it` into LDS buffer `buf`; fetch its LSE/delta to registers.
+  auto load_it = [&](int it, int buf) {
     const int h = g * p.group + it / per_head;
     const int q0 = (qt_first + it % per_head) * kQT;
     const uint16_t* qh = static_cast<const uint16_t*>(p.q) + (size_t)h * p.len_q * D;
     const uint16_t* doh = static_cast<const uint16_t*>(p.d_o) + (size_t)h * p.len_q * D;
-    stq.load(qh, q0, p.len_q, tid);
-    stdo.load(doh, q0, p.len_q, tid);
+    const unsigned bytes = (unsigned)p.len_q * D * 2u;
+    Dma::issue(make_rsrc(qh, bytes), q0, sq[buf], wave, lane);
+    Dma::issue(make_rsrc(doh, bytes), q0, sdo[buf], wave, lane);
     if (tid < kQT) {
       const int row = q0 + tid;
       const bool ok = row < p.len_q;
@@ -94,16 +96,15 @@ __global__ void __launch_bounds__(kNT, 1) bwd_dkdv_kernel(BwdParams p) {
     }
   };
   auto store_it = [&](int buf) {
-    stq.store(sq[buf], tid);
-    stdo.store(sdo[buf], tid);
     if (tid < kQT) slse[buf][tid] = st_lse;
     else if (tid < 2 * kQT) sdel[buf][tid - kQT] = st_del;
   };
 
   if (n_it > 0) {
-    load_it(0);
+    load_it(0, 0);
     store_it(0);
   }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   const float c2 = p.scale_log2;
@@ -112,7 +113,7 @@ __global__ void __launch_bounds__(kNT, 1) bwd_dkdv_kernel(BwdParams p) {
 
   for (int it = 0; it < n_it; ++it) {
     const int buf = it & 1;
-    if (it + 1 < n_it) load_it(it + 1);
+    if (it + 1 < n_it) load_it(it + 1, buf ^ 1);
     const int q0 = (qt_first + it % per_head) * kQT;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -161,6 +162,7 @@ __global__ void __launch_bounds__(kNT, 1) bwd_dkdv_kernel(BwdParams p) {
           dkt[nb] = mfma32x32x16(tile_col8<D>(sq[buf], 32 * b + 16 * q, 32 * nb, lane), dsb[q], dkt[nb]);
     }
     if (it + 1 < n_it) store_it(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
@@ -186,7 +188,7 @@ __global__ void __launch_bounds__(kNT, 1) bwd_dkdv_kernel(BwdParams p) {
 }
 
 template <int D>
-__global__ void __launch_bounds__(kNT, 1) bwd_dq_kernel(BwdParams p) {
+__global__ void __launch_bounds__(kNT, 2) bwd_dq_kernel(BwdParams p) {
   constexpr int KS = D / 16, NB = D / 32, BM = 32 * kNW;
   __shared__ __attribute__((aligned(16))) uint16_t sk[2][kKT * D];
   __shared__ __attribute__((aligned(16))) uint16_t sv[2][kKT * D];
@@ -226,18 +228,19 @@ __global__ void __launch_bounds__(kNT, 1) bwd_dq_kernel(BwdParams p) {
 
   const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (size_t)g * p.len_kv * D;
   const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (size_t)g * p.len_kv * D;
-  TileStager<D, kKT, kNT> stk, stv;
+  using Dma = TileDma<D, kKT, kNT>;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg, (unsigned)p.len_kv * D * 2u);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg, (unsigned)p.len_kv * D * 2u);
 
   f32x16_t dqt[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) dqt[nb] = f32x16_t{};
 
   if (n_kt > 0) {
-    stk.load(kg, 0, p.len_kv, tid);
-    stv.load(vg, 0, p.len_kv, tid);
-    stk.store(sk[0], tid);
-    stv.store(sv[0], tid);
+    Dma::issue(rk, 0, sk[0], wave, lane);
+    Dma::issue(rv, 0, sv[0], wave, lane);
   }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   const float c2 = p.scale_log2;
@@ -247,8 +250,8 @@ __global__ void __launch_bounds__(kNT, 1) bwd_dq_kernel(BwdParams p) {
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < n_kt) {
-      stk.load(kg, (kt + 1) * kKT, p.len_kv, tid);
-      stv.load(vg, (kt + 1) * kKT, p.len_kv, tid);
+      Dma::issue(rk, (kt + 1) * kKT, sk[buf ^ 1], wave, lane);
+      Dma::issue(rv, (kt + 1) * kKT, sv[buf ^ 1], wave, lane);
     }
     const int key0 = kt * kKT;
     const bool wave_visible = !p.causal || key0 - (wave_row0 + 31) <= dpos;
@@ -289,10 +292,7 @@ __global__ void __launch_bounds__(kNT, 1) bwd_dq_kernel(BwdParams p) {
             dqt[nb] = mfma32x32x16(tile_col8<D>(sk[buf], 32 * blk + 16 * q, 32 * nb, lane), dsb[q], dqt[nb]);
       }
     }
-    if (kt + 1 < n_kt) {
-      stk.store(sk[buf ^ 1], tid);
-      stv.store(sv[buf ^ 1], tid);
-    }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
