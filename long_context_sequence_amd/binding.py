@@ -13,7 +13,9 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcp_attn.so")
+# The in-tree build; CP_ATTN_LIB may point at another build of the same sources (development).
+_LIB_PATH = os.environ.get("CP_ATTN_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libcp_attn.so")
 
 CP_OK, CP_STEP_SKIPPED = 0, 1
 CP_F32, CP_BF16 = 0, 1

@@ -34,9 +34,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libcp_attn.so)")
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, verbose: bool, build_dir: str, defines) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *HIP_FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src),
+           "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(line for line in (res.stdout + res.stderr).splitlines()
                     if "packed-fp32-ops" not in line)
@@ -47,18 +48,27 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile and link the library to `out` (default: the in-tree libcp_attn.so). `defines`
+    override compile-time launch shapes (e.g. "CP_FWD_WAVES=8") for experiments."""
+    build_dir = BUILD if out == LIB else out + ".objs"
+    os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, defines), SOURCES))
+    tmp = out + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"linking failed:\n{' '.join(cmd)}\n{res.stdout}{res.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import argparse
+
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", default=LIB)
+    ap.add_argument("-D", dest="defines", action="append", default=[])
+    a = ap.parse_args()
+    print(build(verbose=True, out=os.path.abspath(a.out), defines=a.defines))

@@ -3,11 +3,13 @@
 // forward LSE (P = exp(s - LSE)) rather than stored, and delta = rowsum(dO * O) from the prep
 // kernel standing in for sum_j P_ij dP_ij.
 //
-// Two kernels, no atomics (every output element has one owner workgroup):
-//  * dkdv: a workgroup owns 128 keys of one key/value head (32 per wave, held in registers as
-//    MFMA operands) and streams the query tiles of every query head of its group through LDS:
-//      S = Q K^T, P = exp2(S*scale*log2e - LSE*log2e), dP = dO V^T, dS = P (dP - delta),
-//      dV^T += dO^T P,  dK^T += Q^T dS     (the group's heads summed in registers).
+// Three kernels, no atomics (every output element has one owner workgroup):
+//  * kv (dV part, then dK part): a workgroup owns 128 keys of one key/value head (32 per wave,
+//    held in registers as MFMA operands) and streams the query tiles of every query head of its
+//    group through LDS:
+//      S = Q K^T, P = exp2(S*scale*log2e - LSE*log2e)         dV^T += dO^T P      (dV part)
+//      S, P, dP = dO V^T, dS = P (dP - delta)                  dK^T += Q^T dS      (dK part)
+//    (the group's heads summed in registers).
 //  * dq: a workgroup owns 128 query rows of one head (32 per wave) and streams key/value tiles:
 //      S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T.
 // Transposed operands (dO^T, Q^T, K^T) come from the same row-major LDS tiles through the
@@ -25,9 +27,15 @@ constexpr int kKT = 64;    // keys per tile (dq)
 constexpr int kNW = 4;     // waves per workgroup
 constexpr int kNT = 64 * kNW;
 
-template <int D>
-__global__ void __launch_bounds__(kNT, 1) bwd_dkdv_kernel(BwdParams p) {
+// PART selects the products: kPartDV = S, P, dV^T += dO^T P (K operand only, LSE only);
+// kPartDK = S, dP, dS, dK^T += Q^T dS (K and V operands, LSE and delta). Splitting dV from dK
+// recomputes S once more but halves the accumulators, so each kernel runs two waves per SIMD.
+constexpr int kPartDV = 1, kPartDK = 2;
+
+template <int D, int PART>
+__global__ void __launch_bounds__(kNT, 2) bwd_kv_kernel(BwdParams p) {
   constexpr int KS = D / 16, NB = D / 32, BNK = 32 * kNW;
+  constexpr bool DV = PART == kPartDV;
   __shared__ __attribute__((aligned(16))) uint16_t sq[2][kQT * D];
   __shared__ __attribute__((aligned(16))) uint16_t sdo[2][kQT * D];
   __shared__ __attribute__((aligned(16))) float slse[2][kQT];
@@ -47,13 +55,15 @@ __global__ void __launch_bounds__(kNT, 1) bwd_dkdv_kernel(BwdParams p) {
   const int key_c = k_ok ? key : p.len_kv - 1;
   const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (size_t)g * p.len_kv * D;
   const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (size_t)g * p.len_kv * D;
-  u32x4_t kb[KS], vb[KS];
+  u32x4_t kb[KS], vb[DV ? 1 : KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const u32x4_t xk = *reinterpret_cast<const u32x4_t*>(kg + (size_t)key_c * D + 16 * ks + 8 * half);
-    const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(vg + (size_t)key_c * D + 16 * ks + 8 * half);
     kb[ks] = k_ok ? xk : u32x4_t{0u, 0u, 0u, 0u};
-    vb[ks] = k_ok ? xv : u32x4_t{0u, 0u, 0u, 0u};
+    if constexpr (!DV) {
+      const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(vg + (size_t)key_c * D + 16 * ks + 8 * half);
+      vb[ks] = k_ok ? xv : u32x4_t{0u, 0u, 0u, 0u};
+    }
   }
 
   // Query tiles that see at least one key of this workgroup.
@@ -66,12 +76,9 @@ __global__ void __launch_bounds__(kNT, 1) bwd_dkdv_kernel(BwdParams p) {
   const int per_head = n_qt - qt_first;
   const int n_it = per_head * p.group;
 
-  f32x16_t dkt[NB], dvt[NB];
+  f32x16_t acc[NB];  // dV^T or dK^T of the wave's 32 keys
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    dkt[nb] = f32x16_t{};
-    dvt[nb] = f32x16_t{};
-  }
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16_t{};
 
   using Dma = TileDma<D, kQT, kNT>;
   float st_lse = 0.f, st_del = 0.f;
@@ -90,14 +97,14 @@ __global__ void __launch_bounds__(kNT, 1) bwd_dkdv_kernel(BwdParams p) {
       const float l = ok ? p.lse[(size_t)h * p.len_q + row] : -INFINITY;
       // rows past the end or with no visible key anywhere get P = 0
       st_lse = l == -INFINITY ? INFINITY : l * kLog2e;
-    } else if (tid < 2 * kQT) {
+    } else if (!DV && tid < 2 * kQT) {
       const int row = q0 + tid - kQT;
       st_del = row < p.len_q ? p.delta[(size_t)h * p.len_q + row] : 0.f;
     }
   };
   auto store_it = [&](int buf) {
     if (tid < kQT) slse[buf][tid] = st_lse;
-    else if (tid < 2 * kQT) sdel[buf][tid - kQT] = st_del;
+    else if (!DV && tid < 2 * kQT) sdel[buf][tid - kQT] = st_del;
   };
 
   if (n_it > 0) {
@@ -122,44 +129,41 @@ __global__ void __launch_bounds__(kNT, 1) bwd_dkdv_kernel(BwdParams p) {
       if (p.causal && wave_key0 - (brow + 31) > dpos) continue;
       // some key of the wave invisible to the block's first row: mask
       const bool need_mask = p.causal && wave_key0 + 31 - brow > dpos;
-      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
       const int arow = 32 * b + perm_row(col);
+      // S and dP chains interleaved (independent accumulators)
+      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      for (int ks = 0; ks < KS; ++ks) {
         s = mfma32x32x16(tile_row8<D>(sq[buf], arow, 2 * ks + half), kb[ks], s);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        dp = mfma32x32x16(tile_row8<D>(sdo[buf], arow, 2 * ks + half), vb[ks], dp);
-      u32x4_t pb[2], dsb[2];
+        if constexpr (!DV)
+          dp = mfma32x32x16(tile_row8<D>(sdo[buf], arow, 2 * ks + half), vb[ks], dp);
+      }
+      u32x4_t pb[2];  // P (dV part) or dS (dK part), bf16
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         // accumulator registers 4*a4 .. 4*a4+3 hold 4 consecutive query rows of the tile
         const int rbase = 32 * b + 16 * (a4 >> 1) + 8 * half + 4 * (a4 & 1);
         const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(&slse[buf][rbase]);
-        const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&sdel[buf][rbase]);
-        float pv[4], dsv[4];
+        f32x4_t d4;
+        if constexpr (!DV) d4 = *reinterpret_cast<const f32x4_t*>(&sdel[buf][rbase]);
+        float v4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * a4 + e], c2, -l4[e]));
           if (need_mask && key - (q0 + rbase + e) > dpos) pr = 0.f;
-          pv[e] = pr;
-          dsv[e] = pr * (dp[4 * a4 + e] - d4[e]);
+          if constexpr (DV) v4[e] = pr;
+          else v4[e] = pr * (dp[4 * a4 + e] - d4[e]);
         }
-        pb[a4 >> 1][2 * (a4 & 1)] = pack_bf16x2(pv[0], pv[1]);
-        pb[a4 >> 1][2 * (a4 & 1) + 1] = pack_bf16x2(pv[2], pv[3]);
-        dsb[a4 >> 1][2 * (a4 & 1)] = pack_bf16x2(dsv[0], dsv[1]);
-        dsb[a4 >> 1][2 * (a4 & 1) + 1] = pack_bf16x2(dsv[2], dsv[3]);
+        pb[a4 >> 1][2 * (a4 & 1)] = pack_bf16x2(v4[0], v4[1]);
+        pb[a4 >> 1][2 * (a4 & 1) + 1] = pack_bf16x2(v4[2], v4[3]);
       }
+      // dV^T += dO^T P  or  dK^T += Q^T dS (transposed operand via the transpose read)
+      const uint16_t* tt = DV ? sdo[buf] : sq[buf];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+      for (int q = 0; q < 2; ++q)
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-          dvt[nb] = mfma32x32x16(tile_col8<D>(sdo[buf], 32 * b + 16 * q, 32 * nb, lane), pb[q], dvt[nb]);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-          dkt[nb] = mfma32x32x16(tile_col8<D>(sq[buf], 32 * b + 16 * q, 32 * nb, lane), dsb[q], dkt[nb]);
+        for (int nb = 0; nb < NB; ++nb)
+          acc[nb] = mfma32x32x16(tile_col8<D>(tt, 32 * b + 16 * q, 32 * nb, lane), pb[q], acc[nb]);
     }
     if (it + 1 < n_it) store_it(buf ^ 1);
     __builtin_amdgcn_s_waitcnt(0);
@@ -167,23 +171,17 @@ __global__ void __launch_bounds__(kNT, 1) bwd_dkdv_kernel(BwdParams p) {
   }
 
   if (!k_ok) return;
-  float* dkr = p.dk + ((size_t)g * p.len_kv + key) * D;
-  float* dvr = p.dv + ((size_t)g * p.len_kv + key) * D;
+  float* out = (DV ? p.dv : p.dk) + ((size_t)g * p.len_kv + key) * D;
+  const float f = DV ? 1.f : p.scale;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
-      const int n = 32 * nb + 8 * a4 + 4 * half;
-      f32x4_t* pk = reinterpret_cast<f32x4_t*>(dkr + n);
-      f32x4_t* pv = reinterpret_cast<f32x4_t*>(dvr + n);
-      f32x4_t ok4 = *pk, ov4 = *pv;
+      f32x4_t* ptr = reinterpret_cast<f32x4_t*>(out + 32 * nb + 8 * a4 + 4 * half);
+      f32x4_t o4 = *ptr;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ok4[e] += p.scale * dkt[nb][4 * a4 + e];
-        ov4[e] += dvt[nb][4 * a4 + e];
-      }
-      *pk = ok4;
-      *pv = ov4;
+      for (int e = 0; e < 4; ++e) o4[e] += f * acc[nb][4 * a4 + e];
+      *ptr = o4;
     }
 }
 
@@ -263,11 +261,10 @@ __global__ void __launch_bounds__(kNT, 2) bwd_dq_kernel(BwdParams p) {
         f32x16_t s = f32x16_t{}, dp = f32x16_t{};
         const int arow = 32 * blk + perm_row(col);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int ks = 0; ks < KS; ++ks) {  // S^T and dP^T chains interleaved
           s = mfma32x32x16(tile_row8<D>(sk[buf], arow, 2 * ks + half), qb[ks], s);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
           dp = mfma32x32x16(tile_row8<D>(sv[buf], arow, 2 * ks + half), dob[ks], dp);
+        }
         u32x4_t dsb[2];
 #pragma unroll
         for (int r2 = 0; r2 < 8; ++r2) {
@@ -286,9 +283,9 @@ __global__ void __launch_bounds__(kNT, 2) bwd_dq_kernel(BwdParams p) {
           dsb[r2 >> 2][r2 & 3] = pack_bf16x2(dsv[0], dsv[1]);
         }
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        for (int q = 0; q < 2; ++q)
 #pragma unroll
-          for (int q = 0; q < 2; ++q)
+          for (int nb = 0; nb < NB; ++nb)
             dqt[nb] = mfma32x32x16(tile_col8<D>(sk[buf], 32 * blk + 16 * q, 32 * nb, lane), dsb[q], dqt[nb]);
       }
     }
@@ -314,9 +311,13 @@ template <int D>
 hipError_t launch_d(const BwdParams& p, int which, hipStream_t s) {
   if (which & 1) {
     const int n_kt = (p.len_kv + 32 * kNW - 1) / (32 * kNW);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)(n_kt * p.heads_kv)), dim3(kNT), 0,
-                       s, p);
-    const hipError_t e = hipGetLastError();
+    hipLaunchKernelGGL((bwd_kv_kernel<D, kPartDV>), dim3((unsigned)(n_kt * p.heads_kv)), dim3(kNT),
+                       0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_kv_kernel<D, kPartDK>), dim3((unsigned)(n_kt * p.heads_kv)), dim3(kNT),
+                       0, s, p);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (which & 2) {

@@ -17,8 +17,10 @@
 // cover 8 consecutive keys, so the matching V^T operand is one transpose read (two
 // ds_read_b64_tr_b16) of the row-major V tile.
 //
-// Causality: a tile is computed only if some key in it is visible to some row of the wave;
-// the mask is applied only on tiles that straddle the diagonal or the ragged end of the chunk.
+// Causality: the workgroup visits only tiles some of its rows can see; the mask is applied only
+// on tiles that straddle the diagonal (for the wave's rows) or the ragged end of the chunk.
+// Pipelining: S of the next tile is computed on the matrix cores while the VALU turns the
+// current tile's S into P, so each wave keeps both busy.
 #include <math.h>
 
 #include "device_common.hpp"
@@ -27,13 +29,20 @@
 namespace cpa {
 namespace {
 
-constexpr int kBN = 64;       // keys per tile
+// Launch shape: waves per workgroup (32 query rows each) and keys per LDS tile.
+#ifndef CP_FWD_WAVES
+#define CP_FWD_WAVES 4
+#endif
+#ifndef CP_FWD_KEYS
+#define CP_FWD_KEYS 64
+#endif
 constexpr float kTau = 8.f;   // the reference max moves only when a row max grows by more than
                               // this (log2 units): P stays <= 2^8 and most tiles skip the rescale
 
-template <int D, int NW>
+template <int D, int NW, int kBN>
 __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(StepParams p) {
   constexpr int NT = NW * 64, BM = 32 * NW, KS = D / 16, NB = D / 32;
+  constexpr int SB = kBN / 32;  // 32-key blocks per tile
   __shared__ __attribute__((aligned(16))) uint16_t sk[2][kBN * D];
   __shared__ __attribute__((aligned(16))) uint16_t sv[2][kBN * D];
 
@@ -85,88 +94,104 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(StepParams p) {
   float m_run = -INFINITY;  // reference row max of scale*log2(e)*s
   float l_run = 0.f;        // this lane's share of the running row sum
 
+  const float c2 = p.scale_log2;
+
+  // S^T = K Q^T of one tile from an LDS buffer; consecutive MFMAs go to different 32-key blocks
+  // (independent accumulators).
+  auto scores = [&](const uint16_t* kt_lds, f32x16_t (&sc)[SB]) {
+#pragma unroll
+    for (int blk = 0; blk < SB; ++blk) sc[blk] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int blk = 0; blk < SB; ++blk)
+        sc[blk] = mfma32x32x16(tile_row8<D>(kt_lds, 32 * blk + perm_row(col), 2 * ks + half),
+                               qreg[ks], sc[blk]);
+  };
+
+  // Software pipeline over key tiles, K one tile ahead of V. During iteration j the wave holds
+  // S_j (computed in iteration j-1) and, while the VALU turns S_j into P_j, the matrix cores
+  // compute S_{j+1}; then O += V_j^T P_j. LDS: K_{j+1} and V_j are resident; the direct loads of
+  // K_{j+2} (into K_j's buffer) and V_{j+1} (into V_{j-1}'s) are in flight.
+  f32x16_t s_cur[SB];
   if (n_kt > 0) {
     Dma::issue(rk, 0, sk[0], wave, lane);
     Dma::issue(rv, 0, sv[0], wave, lane);
+    if (n_kt > 1) Dma::issue(rk, kBN, sk[1], wave, lane);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    scores(sk[0], s_cur);
+    __syncthreads();  // every wave is done with K_0 before K_2 lands in its buffer
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  const float c2 = p.scale_log2;
 
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < n_kt) {
-      Dma::issue(rk, (kt + 1) * kBN, sk[buf ^ 1], wave, lane);
-      Dma::issue(rv, (kt + 1) * kBN, sv[buf ^ 1], wave, lane);
-    }
+    if (kt + 1 < n_kt) Dma::issue(rv, (kt + 1) * kBN, sv[buf ^ 1], wave, lane);
+    if (kt + 2 < n_kt) Dma::issue(rk, (kt + 2) * kBN, sk[buf], wave, lane);
     const int key0 = kt * kBN;
-    // some key of the tile visible to the wave's last row?
-    const bool wave_visible = !p.causal || key0 - (wave_row0 + 31) <= dpos;
-    if (wave_visible) {
-      f32x16_t s[2];
+    // every key of the tile visible to the wave's first row and inside the chunk?
+    const bool full = key0 + kBN <= p.len_kv && (!p.causal || key0 + kBN - 1 - wave_row0 <= dpos);
+    if (!full) {
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        s[blk] = f32x16_t{};
-        const int row = 32 * blk + perm_row(col);
+      for (int blk = 0; blk < SB; ++blk)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          s[blk] = mfma32x32x16(tile_row8<D>(sk[buf], row, 2 * ks + half), qreg[ks], s[blk]);
-      }
-      // every key of the tile visible to the wave's first row and inside the chunk?
-      const bool full = key0 + kBN <= p.len_kv && (!p.causal || key0 + kBN - 1 - wave_row0 <= dpos);
-      if (!full) {
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * blk + perm_row(8 * (r >> 2) + 4 * half + (r & 3));
+          const bool vis = (key < p.len_kv) & ((!p.causal) | (key - qi <= dpos));
+          s_cur[blk][r] = vis ? s_cur[blk][r] : -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
+    for (int blk = 0; blk < SB; ++blk)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + 32 * blk + perm_row(8 * (r >> 2) + 4 * half + (r & 3));
-            const bool vis = (key < p.len_kv) & ((!p.causal) | (key - qi <= dpos));
-            s[blk][r] = vis ? s[blk][r] : -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[blk][r]);
-      mx = pair_max(mx) * c2;
-      // Move the reference max only when the row max outgrew it by more than kTau (the first
-      // visible tile always does: m_run starts at -inf). P = exp2(s*c2 - m_run) <= 2^kTau.
-      const bool grow = mx > m_run + kTau;
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
-      m_run = grow ? mx : m_run;
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-
-      // P in bf16 as the PV operand; the row sum (and so the LSE) from the fp32 values.
-      u32x4_t pb[4];
-      float lsum = 0.f;
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][8 * q + 2 * t], c2, -m_use));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][8 * q + 2 * t + 1], c2, -m_use));
-            pb[2 * blk + q][t] = pack_bf16x2(p0, p1);
-            lsum += p0 + p1;
-          }
-      l_run = l_run * alpha + lsum;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[nb][r] *= alpha;
-      }
-      // O^T += V^T P^T: the V^T operand for keys 16*kk .. 16*kk+15 via the transpose read.
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[blk][r]);
+    mx = pair_max(mx) * c2;
+    // Move the reference max only when the row max outgrew it by more than kTau (the first
+    // visible tile always does: m_run starts at -inf). P = exp2(s*c2 - m_run) <= 2^kTau.
+    const bool grow = mx > m_run + kTau;
+    const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
+    m_run = grow ? mx : m_run;
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          oacc[nb] = mfma32x32x16(tile_col8<D>(sv[buf], 16 * kk, 32 * nb, lane), pb[kk], oacc[nb]);
+        for (int r = 0; r < 16; ++r) oacc[nb][r] *= alpha;
     }
-    // the next tile's direct loads have landed, and every wave is done with this one
+
+    // S_{j+1} on the matrix cores (independent of what follows) ... Unconditional so that it
+    // shares a basic block with the exp work below; on the last tile it reads the other (stale
+    // but in-bounds) K buffer and the result is discarded.
+    f32x16_t s_nxt[SB];
+    scores(sk[buf ^ 1], s_nxt);
+
+    // ... while P_j = exp2(S_j*c2 - m) goes to bf16 (PV operand); the row sum stays fp32.
+    u32x4_t pb[2 * SB];
+    float lsum = 0.f;
+#pragma unroll
+    for (int blk = 0; blk < SB; ++blk)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[blk][8 * q + 2 * t], c2, -m_use));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[blk][8 * q + 2 * t + 1], c2, -m_use));
+          pb[2 * blk + q][t] = pack_bf16x2(p0, p1);
+          lsum += p0 + p1;
+        }
+    l_run = l_run * alpha + lsum;
+
+    // O^T += V^T P^T: the V^T operand for keys 16*kk .. 16*kk+15 via the transpose read.
+#pragma unroll
+    for (int kk = 0; kk < 2 * SB; ++kk)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        oacc[nb] = mfma32x32x16(tile_col8<D>(sv[buf], 16 * kk, 32 * nb, lane), pb[kk], oacc[nb]);
+
+#pragma unroll
+    for (int blk = 0; blk < SB; ++blk) s_cur[blk] = s_nxt[blk];
+    // V_{j+1} and K_{j+2} have landed and every wave is done with V_j and K_{j+1}
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
@@ -219,10 +244,10 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(StepParams p) {
 
 template <int D>
 hipError_t launch_d(const StepParams& p, hipStream_t s) {
-  constexpr int NW = 4;
+  constexpr int NW = CP_FWD_WAVES, BN = CP_FWD_KEYS;
   const int n_qt = (p.len_q + 32 * NW - 1) / (32 * NW);
   const dim3 grid((unsigned)(n_qt * p.heads_q));
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW>), grid, dim3(NW * 64), 0, s, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BN>), grid, dim3(NW * 64), 0, s, p);
   return hipGetLastError();
 }
 
