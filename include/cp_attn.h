@@ -185,6 +185,34 @@ cp_status cp_attn_ring_bwd(const cp_ring_desc* ring, const void* q, const void* 
                            const float* lse, float* delta_work, float* dq, float* dk_chunks,
                            float* dv_chunks, void* stream);
 
+/*
+ * Zig-zag causal load balancing (context-parallelism page, section 5: Llama 3's split, which
+ * StripedHyena 2 also trains with): the sequence is cut into 2 * n_cp half-chunks x_0 ..
+ * x_{2 n_cp - 1} of Lh rows and rank r holds x_r and x_{2 n_cp - 1 - r}, so every rank gets the
+ * same causal work. Layout of a rank's tensors is half-major: q, d_o, o, dq [2, heads, Lh, d]
+ * (index 0 = x_r, 1 = x_{2 n_cp - 1 - r}); lse, delta [2, heads, Lh]; the chunk a rank passes
+ * around is its pair of halves, so k_chunks, v_chunks, dk_chunks, dv_chunks are
+ * [n_cp, 2, heads_kv, Lh, d]. ring->chunk_len is Lh (the half-chunk length).
+ */
+
+/* cp_zigzag_shards — the two half-chunk indices rank `rank` holds (shards[0] < shards[1]).
+ * Returns 0, or a negative cp_status. Host only. */
+int32_t cp_zigzag_shards(int32_t n_cp, int32_t rank, int32_t* shards);
+
+/* cp_attn_ring_fwd_zigzag — the rank's forward over all ring steps under the zig-zag split:
+ * at step s it holds rank (rank - s) mod n_cp's pair of halves and runs cp_attn_step for each
+ * (query half, key/value half) pair that is not causally empty, folding into o/lse. */
+cp_status cp_attn_ring_fwd_zigzag(const cp_ring_desc* ring, const void* q, const void* k_chunks,
+                                  const void* v_chunks, float* o, float* lse, void* stream);
+
+/* cp_attn_ring_bwd_zigzag — the matching backward: delta prep over both halves, then
+ * cp_attn_bwd for every non-empty (query half, key/value half) pair. dq, dk_chunks, dv_chunks
+ * are accumulated (+=). delta_work: [2, heads_q, Lh] fp32 scratch. */
+cp_status cp_attn_ring_bwd_zigzag(const cp_ring_desc* ring, const void* q, const void* k_chunks,
+                                  const void* v_chunks, const void* d_o, const float* o,
+                                  const float* lse, float* delta_work, float* dq,
+                                  float* dk_chunks, float* dv_chunks, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* cp_attn_status_string(int32_t status);
 

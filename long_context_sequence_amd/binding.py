@@ -82,6 +82,13 @@ def load():
     lib.cp_attn_ring_bwd.argtypes = [ctypes.POINTER(RingDesc), _P, _P, _P, _P, _P, _P, _P, _P,
                                      _P, _P, _P]
     lib.cp_attn_ring_bwd.restype = st
+    lib.cp_zigzag_shards.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
+    lib.cp_zigzag_shards.restype = ctypes.c_int32
+    lib.cp_attn_ring_fwd_zigzag.argtypes = [ctypes.POINTER(RingDesc), _P, _P, _P, _P, _P, _P]
+    lib.cp_attn_ring_fwd_zigzag.restype = st
+    lib.cp_attn_ring_bwd_zigzag.argtypes = [ctypes.POINTER(RingDesc), _P, _P, _P, _P, _P, _P, _P,
+                                            _P, _P, _P, _P]
+    lib.cp_attn_ring_bwd_zigzag.restype = st
     lib.cp_attn_status_string.argtypes = [ctypes.c_int32]
     lib.cp_attn_status_string.restype = ctypes.c_char_p
     lib.cp_attn_abi_version.argtypes = []
@@ -267,3 +274,58 @@ def ring_bwd(q, k_chunks, v_chunks, d_o, o, lse, delta_work, dq, dk_chunks, dv_c
                                           _ptr(d_o), _ptr(o), _ptr(lse), _ptr(delta_work), _ptr(dq),
                                           _ptr(dk_chunks), _ptr(dv_chunks), _stream()),
                   "cp_attn_ring_bwd", allow_skip=False)
+
+
+def zigzag_shards(n_cp: int, rank: int):
+    """cp_zigzag_shards: the two half-chunk indices a rank holds (host only)."""
+    out = (ctypes.c_int32 * 2)()
+    st = load().cp_zigzag_shards(int(n_cp), int(rank), out)
+    if st < 0:
+        raise CpAttnError(st, "cp_zigzag_shards")
+    return int(out[0]), int(out[1])
+
+
+def _ring_zz(q, k_chunks, rank, causal, scale):
+    _, hq, lh, d = q.shape
+    n_cp, _, hkv = k_chunks.shape[:3]
+    return RingDesc(hq, hkv, lh, d, n_cp, int(rank), int(bool(causal)),
+                    float(scale) if scale else 0.0, _dtype_code(q))
+
+
+def ring_fwd_zigzag(q, k_chunks, v_chunks, o, lse, rank, causal, scale=None):
+    """cp_attn_ring_fwd_zigzag: q [2, H_q, Lh, d]; k_chunks, v_chunks [N_cp, 2, H_kv, Lh, d];
+    o [2, H_q, Lh, d] fp32; lse [2, H_q, Lh] fp32 (half-major layout)."""
+    _need(q, "q")
+    if q.dim() != 4 or q.shape[0] != 2:
+        raise ValueError("q must be [2, H_q, Lh, d]")
+    n_cp = k_chunks.shape[0]
+    _need(k_chunks, "k_chunks", shape=(n_cp, 2, k_chunks.shape[2], q.shape[2], q.shape[3]),
+          dtype=q.dtype)
+    _need(v_chunks, "v_chunks", shape=k_chunks.shape, dtype=q.dtype)
+    _need(o, "o", shape=q.shape, dtype=torch.float32)
+    _need(lse, "lse", shape=q.shape[:3], dtype=torch.float32)
+    r = _ring_zz(q, k_chunks, rank, causal, scale)
+    return _check(load().cp_attn_ring_fwd_zigzag(ctypes.byref(r), _ptr(q), _ptr(k_chunks),
+                                                 _ptr(v_chunks), _ptr(o), _ptr(lse), _stream()),
+                  "cp_attn_ring_fwd_zigzag", allow_skip=False)
+
+
+def ring_bwd_zigzag(q, k_chunks, v_chunks, d_o, o, lse, delta_work, dq, dk_chunks, dv_chunks,
+                    rank, causal, scale=None):
+    """cp_attn_ring_bwd_zigzag (half-major layout); dq, dk_chunks, dv_chunks accumulated."""
+    _need(q, "q")
+    _need(k_chunks, "k_chunks", dtype=q.dtype)
+    _need(v_chunks, "v_chunks", shape=k_chunks.shape, dtype=q.dtype)
+    _need(d_o, "d_o", shape=q.shape, dtype=q.dtype)
+    _need(o, "o", shape=q.shape, dtype=torch.float32)
+    _need(lse, "lse", shape=q.shape[:3], dtype=torch.float32)
+    _need(delta_work, "delta_work", shape=q.shape[:3], dtype=torch.float32)
+    _need(dq, "dq", shape=q.shape, dtype=torch.float32)
+    _need(dk_chunks, "dk_chunks", shape=k_chunks.shape, dtype=torch.float32)
+    _need(dv_chunks, "dv_chunks", shape=k_chunks.shape, dtype=torch.float32)
+    r = _ring_zz(q, k_chunks, rank, causal, scale)
+    return _check(load().cp_attn_ring_bwd_zigzag(ctypes.byref(r), _ptr(q), _ptr(k_chunks),
+                                                 _ptr(v_chunks), _ptr(d_o), _ptr(o), _ptr(lse),
+                                                 _ptr(delta_work), _ptr(dq), _ptr(dk_chunks),
+                                                 _ptr(dv_chunks), _stream()),
+                  "cp_attn_ring_bwd_zigzag", allow_skip=False)

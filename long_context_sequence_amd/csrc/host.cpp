@@ -330,4 +330,93 @@ cp_status cp_attn_ring_bwd(const cp_ring_desc* ring, const void* q, const void* 
   return CP_OK;
 }
 
+int32_t cp_zigzag_shards(int32_t n_cp, int32_t rank, int32_t* shards) {
+  if (!shards) return CP_ERR_NULL;
+  if (n_cp < 1 || n_cp > kMaxRing || rank < 0 || rank >= n_cp) return CP_ERR_SHAPE;
+  shards[0] = rank;
+  shards[1] = 2 * n_cp - 1 - rank;
+  return 0;
+}
+
+cp_status cp_attn_ring_fwd_zigzag(const cp_ring_desc* ring, const void* q, const void* k_chunks,
+                                  const void* v_chunks, float* o, float* lse, void* stream) {
+  cp_status st = check_ring(ring);
+  if (st != CP_OK) return st;
+  cp_attn_desc d0 = ring_step_desc(ring, ring->rank, 0);
+  st = check_desc(&d0);
+  if (st != CP_OK) return st;
+  st = check_ptrs({q, k_chunks, v_chunks, o, lse});
+  if (st != CP_OK) return st;
+  const int32_t n = ring->n_cp, lh = ring->chunk_len;
+  const size_t esz = elem_size(ring->dtype);
+  const size_t q_half = (size_t)ring->heads_q * lh * ring->head_dim;    // elements
+  const size_t kv_half = (size_t)ring->heads_kv * lh * ring->head_dim;
+  const int64_t rows_half = (int64_t)ring->heads_q * lh;
+  const int32_t qs[2] = {ring->rank, 2 * n - 1 - ring->rank};
+  bool started[2] = {false, false};
+  for (int32_t s = 0; s < n; ++s) {
+    const int32_t c = ((ring->rank - s) % n + n) % n;
+    const int32_t ks[2] = {c, 2 * n - 1 - c};
+    for (int a = 0; a < 2; ++a) {
+      for (int b = 0; b < 2; ++b) {
+        cp_attn_desc d = d0;
+        d.q_pos0 = (int64_t)qs[a] * lh;
+        d.kv_pos0 = (int64_t)ks[b] * lh;
+        if (causally_empty(&d)) continue;
+        d.accumulate = started[a] ? 1 : 0;
+        const char* kb = static_cast<const char*>(k_chunks) + ((size_t)c * 2 + b) * kv_half * esz;
+        const char* vb = static_cast<const char*>(v_chunks) + ((size_t)c * 2 + b) * kv_half * esz;
+        st = cp_attn_step(&d, static_cast<const char*>(q) + a * q_half * esz, kb, vb,
+                          o + a * q_half, lse + a * rows_half, stream);
+        if (st != CP_OK && st != CP_STEP_SKIPPED) return st;
+        started[a] = true;
+      }
+    }
+  }
+  return CP_OK;
+}
+
+cp_status cp_attn_ring_bwd_zigzag(const cp_ring_desc* ring, const void* q, const void* k_chunks,
+                                  const void* v_chunks, const void* d_o, const float* o,
+                                  const float* lse, float* delta_work, float* dq,
+                                  float* dk_chunks, float* dv_chunks, void* stream) {
+  cp_status st = check_ring(ring);
+  if (st != CP_OK) return st;
+  cp_attn_desc d0 = ring_step_desc(ring, ring->rank, 0);
+  st = check_desc(&d0);
+  if (st != CP_OK) return st;
+  if (ring->dtype != CP_BF16) return CP_ERR_UNSUPPORTED;
+  st = check_ptrs({q, k_chunks, v_chunks, d_o, o, lse, delta_work, dq, dk_chunks, dv_chunks});
+  if (st != CP_OK) return st;
+  const int32_t n = ring->n_cp, lh = ring->chunk_len;
+  const size_t esz = elem_size(ring->dtype);
+  const size_t q_half = (size_t)ring->heads_q * lh * ring->head_dim;
+  const size_t kv_half = (size_t)ring->heads_kv * lh * ring->head_dim;
+  const int64_t rows_half = (int64_t)ring->heads_q * lh;
+  st = cp_attn_bwd_prep(2 * rows_half, ring->head_dim, ring->dtype, o, d_o, delta_work, stream);
+  if (st != CP_OK) return st;
+  const int32_t qs[2] = {ring->rank, 2 * n - 1 - ring->rank};
+  for (int32_t s = 0; s < n; ++s) {
+    const int32_t c = ((ring->rank - s) % n + n) % n;
+    const int32_t ks[2] = {c, 2 * n - 1 - c};
+    for (int a = 0; a < 2; ++a) {
+      for (int b = 0; b < 2; ++b) {
+        cp_attn_desc d = d0;
+        d.q_pos0 = (int64_t)qs[a] * lh;
+        d.kv_pos0 = (int64_t)ks[b] * lh;
+        if (causally_empty(&d)) continue;
+        const size_t kvo = ((size_t)c * 2 + b) * kv_half;
+        st = cp_attn_bwd(&d, static_cast<const char*>(q) + a * q_half * esz,
+                         static_cast<const char*>(k_chunks) + kvo * esz,
+                         static_cast<const char*>(v_chunks) + kvo * esz,
+                         static_cast<const char*>(d_o) + a * q_half * esz, lse + a * rows_half,
+                         delta_work + a * rows_half, dq + a * q_half, dk_chunks + kvo,
+                         dv_chunks + kvo, stream);
+        if (st != CP_OK && st != CP_STEP_SKIPPED) return st;
+      }
+    }
+  }
+  return CP_OK;
+}
+
 }  // extern "C"

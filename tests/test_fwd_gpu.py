@@ -211,3 +211,47 @@ def test_full_size_sampled_rows(key):
             nvis = r * wl.chunk_len + rows[t] + 1 if wl.causal else wl.seq_len
             s = (kf[g[t], :nvis].astype(np.float64) @ qf[t]) * wl.scale
             assert abs(np.sum(np.exp(s - l_s[t])) - 1.0) < 2e-3
+
+
+def test_ulysses_share_full_sequence_on_local_heads():
+    """The all-to-all (Ulysses) branch of the same method (context-parallelism page, section
+    2; Ulysses explainer, the four-step procedure): after the exchange a GPU holds H/N_cp heads
+    over the whole sequence and runs plain causal attention on them. For the 32K GQA workload
+    at degree 8 that is 4 query heads sharing 1 key/value head over 32,768 tokens: one step with
+    both offsets 0. Checked on sampled rows one by one, plus a full backward at 4K tokens."""
+    hq, hkv, d, L = 4, 1, 128, 32768
+    qa = inputs.make(401, "q", 0, (hq, L, d), "bf16")
+    ka = inputs.make(401, "k", 0, (hkv, L, d), "bf16")
+    va = inputs.make(401, "v", 0, (hkv, L, d), "bf16")
+    q, k, v = (inputs.to_torch(a, "cuda") for a in (qa, ka, va))
+    o = torch.empty(q.shape, device="cuda")
+    lse = torch.empty(q.shape[:2], device="cuda")
+    assert cp.step(q, k, v, o, lse, causal=True) == cp.CP_OK
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    rows = np.concatenate([[0, 1, L - 1], rng.integers(0, L, 13)])
+    heads = rng.integers(0, hq, rows.size)
+    o_ref, l_ref = oracle.attention_rows(inputs.widen(qa)[heads, rows], inputs.widen(ka),
+                                         inputs.widen(va), heads, rows, hq, causal=True)
+    check_o_lse(o[heads, rows].cpu().numpy(), lse[heads, rows].cpu().numpy(), o_ref, l_ref,
+                "bf16", "ulysses share")
+    # backward on a 4K-token prefix against the full oracle
+    n = 4096
+    qs, ks, vs = (t[:, :n].contiguous() for t in (q, k, v))
+    do_a = inputs.make(401, "do", 0, (hq, n, d), "bf16")
+    d_o = inputs.to_torch(do_a, "cuda")
+    o2 = torch.empty(qs.shape, device="cuda")
+    l2 = torch.empty(qs.shape[:2], device="cuda")
+    cp.step(qs, ks, vs, o2, l2, causal=True)
+    delta = torch.empty_like(l2)
+    cp.bwd_prep(o2, d_o, delta)
+    dq = torch.zeros_like(o2)
+    dk = torch.zeros(ks.shape, device="cuda")
+    dv = torch.zeros(vs.shape, device="cuda")
+    cp.bwd(qs, ks, vs, d_o, l2, delta, dq, dk, dv, causal=True)
+    torch.cuda.synchronize()
+    refs = oracle.attention_backward(inputs.widen(qa[:, :n]), inputs.widen(ka[:, :n]),
+                                     inputs.widen(va[:, :n]), inputs.widen(do_a), causal=True)
+    for name, got, ref in zip(("dQ", "dK", "dV"), (dq, dk, dv), refs):
+        err = np.max(np.abs(got.cpu().numpy() - ref))
+        assert err <= 5e-2 * np.max(np.abs(ref)), name
