@@ -116,7 +116,7 @@ def main():
                   file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
 
-    def run_step(ev_f=None, ev_b=None, ev_q=None):
+    def run_step(ev_f=None, ev_b=None):
         first = True
         for i, (c, _) in enumerate(sched):
             if ev_f is not None:
@@ -140,16 +140,10 @@ def main():
             for i, (c, _) in enumerate(sched):
                 if ev_b is not None:
                     ev_b[i][0].record(stream)
-                cp.bwd_dkdv(q, kc[c], vc[c], d_o, lse, delta, dk[c], dv[c], q_pos0=rank * lc,
-                            kv_pos0=c * lc, causal=wl.causal)
+                cp.bwd(q, kc[c], vc[c], d_o, lse, delta, dq, dk[c], dv[c], q_pos0=rank * lc,
+                       kv_pos0=c * lc, causal=wl.causal)
                 if ev_b is not None:
                     ev_b[i][1].record(stream)
-                if ev_q is not None:
-                    ev_q[i][0].record(stream)
-                cp.bwd_dq(q, kc[c], vc[c], d_o, lse, delta, dq, q_pos0=rank * lc,
-                          kv_pos0=c * lc, causal=wl.causal)
-                if ev_q is not None:
-                    ev_q[i][1].record(stream)
 
     for _ in range(args.warmup):
         run_step()
@@ -159,33 +153,29 @@ def main():
     mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     evs_f = [[(mk(), mk()) for _ in sched] for _ in range(args.steps)]
     evs_b = [[(mk(), mk()) for _ in sched] for _ in range(args.steps)]
-    evs_q = [[(mk(), mk()) for _ in sched] for _ in range(args.steps)]
     start, end = mk(), mk()
     torch.cuda.synchronize()
     start.record(stream)
     for s in range(args.steps):
-        run_step(evs_f[s], evs_b[s] if do_bwd else None, evs_q[s] if do_bwd else None)
+        run_step(evs_f[s], evs_b[s] if do_bwd else None)
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / args.steps
     fwd_ms = sum(a.elapsed_time(b) for st in evs_f for a, b in st) / args.steps
-    dkdv_ms = (sum(a.elapsed_time(b) for st in evs_b for a, b in st) / args.steps) if do_bwd else 0.0
-    dq_ms = (sum(a.elapsed_time(b) for st in evs_q for a, b in st) / args.steps) if do_bwd else 0.0
-    bwd_ms = dkdv_ms + dq_ms
+    bwd_ms = (sum(a.elapsed_time(b) for st in evs_b for a, b in st) / args.steps) if do_bwd else 0.0
     f_fwd = sum(fwd_step_flops)
     f_bwd = sum(bwd_step_flops) if do_bwd else 0.0
     print(f"# timed {args.steps} steps: {ms_step:.2f} ms/step (fwd kernels {fwd_ms:.2f} ms, "
-          f"dK/dV kernels {dkdv_ms:.2f} ms, dQ kernels {dq_ms:.2f} ms)", file=sys.stderr,
-          flush=True)
+          f"bwd kernels {bwd_ms:.2f} ms)", file=sys.stderr, flush=True)
 
     # Dominant kernel: the one with the largest share of the step. Algorithmic flops per launch:
-    # forward 4*d*H_q per visible pair (QK^T, PV); dK/dV kernel 8*d*H_q (S recompute, dP, dV,
-    # dK); dQ kernel 6*d*H_q (S, dP, dQ). Summed over the step's launches / summed durations.
+    # forward 4*d*H_q per visible pair (QK^T, PV); backward 10*d*H_q (S recompute, dP, dV, dK,
+    # dQ), one bwd_kernel launch per ring step. Summed over the step's launches / summed
+    # durations.
     cands = [("fwd_bf16_kernel (cp_attn_step)", fwd_ms, f_fwd)]
     if do_bwd:
-        cands.append(("bwd_dkdv_kernel (cp_attn_bwd_dkdv)", dkdv_ms, f_bwd * 0.8))
-        cands.append(("bwd_dq_kernel (cp_attn_bwd_dq)", dq_ms, f_bwd * 0.6))
+        cands.append(("bwd_kernel (cp_attn_bwd)", bwd_ms, f_bwd))
     dom_name, dom_ms, dom_flops = max(cands, key=lambda c: c[1])
     n_launch = len(sched)
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
@@ -225,8 +215,7 @@ def main():
         "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
         "fwd_frac_of_peak": round(f_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2) if do_bwd else None,
-        "kernel_ms_per_step": {"fwd": round(fwd_ms, 3), "bwd_dkdv": round(dkdv_ms, 3),
-                               "bwd_dq": round(dq_ms, 3)},
+        "kernel_ms_per_step": {"fwd": round(fwd_ms, 3), "bwd": round(bwd_ms, 3)},
         "bwd_frac_of_peak": (round(f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
                              if do_bwd else None),
         "tokens_per_s": round(lc / (ms_step * 1e-3), 1),
@@ -237,9 +226,8 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-KERNEL_SOURCES = {"fwd_bf16_kernel": "fwd_bf16.hip", "bwd_dkdv_kernel": "bwd_bf16.hip",
-                  "bwd_dq_kernel": "bwd_bf16.hip", "merge_kernel": "elementwise.hip",
-                  "prep_kernel": "elementwise.hip"}
+KERNEL_SOURCES = {"fwd_bf16_kernel": "fwd_bf16.hip", "bwd_kernel": "bwd_bf16.hip",
+                  "merge_kernel": "elementwise.hip", "prep_kernel": "elementwise.hip"}
 
 
 def measured_traffic(workload_name, kernel):

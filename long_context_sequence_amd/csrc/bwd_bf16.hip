@@ -3,7 +3,7 @@
 // forward LSE (P = exp(s - LSE)) rather than stored, and delta = rowsum(dO * O) from the prep
 // kernel standing in for sum_j P_ij dP_ij.
 //
-// Three kernels, no atomics (every output element has one owner workgroup):
+// Three workgroup kinds in one launch, no atomics (every output element has one owner):
 //  * kv (dV part, then dK part): a workgroup owns 128 keys of one key/value head (32 per wave,
 //    held in registers as MFMA operands) and streams the query tiles of every query head of its
 //    group through LDS:
@@ -32,19 +32,27 @@ constexpr int kNT = 64 * kNW;
 // recomputes S once more but halves the accumulators, so each kernel runs two waves per SIMD.
 constexpr int kPartDV = 1, kPartDK = 2;
 
+// LDS of the kv parts: Q and dO tiles, double buffered, then LSE*log2e and delta per row.
+template <int D>
+constexpr int kv_smem_bytes() { return 2 * 2 * kQT * D * 2 + 2 * 2 * kQT * 4; }
+// LDS of the dQ part: K and V tiles, double buffered.
+template <int D>
+constexpr int dq_smem_bytes() { return 2 * 2 * kKT * D * 2; }
+
 template <int D, int PART>
-__global__ void __launch_bounds__(kNT, 2) bwd_kv_kernel(BwdParams p) {
+__device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* smem) {
   constexpr int KS = D / 16, NB = D / 32, BNK = 32 * kNW;
   constexpr bool DV = PART == kPartDV;
-  __shared__ __attribute__((aligned(16))) uint16_t sq[2][kQT * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sdo[2][kQT * D];
-  __shared__ __attribute__((aligned(16))) float slse[2][kQT];
-  __shared__ __attribute__((aligned(16))) float sdel[2][kQT];
+  uint16_t* const sq_base = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* const sdo_base = sq_base + 2 * kQT * D;
+  float* const slse = reinterpret_cast<float*>(sdo_base + 2 * kQT * D);  // [2][kQT]
+  float* const sdel = slse + 2 * kQT;                                     // [2][kQT]
+  auto SQ = [&](int b) { return sq_base + b * (kQT * D); };
+  auto SDO = [&](int b) { return sdo_base + b * (kQT * D); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
   const int n_kt = (p.len_kv + BNK - 1) / BNK;
-  const int w = xcd_remap(blockIdx.x, n_kt * p.heads_kv);
   const int g = w / n_kt;
   const int kt = w % n_kt;  // ascending: under causality the earliest keys have most work
   const int kv_base = kt * BNK;
@@ -89,8 +97,8 @@ __global__ void __launch_bounds__(kNT, 2) bwd_kv_kernel(BwdParams p) {
     const uint16_t* qh = static_cast<const uint16_t*>(p.q) + (size_t)h * p.len_q * D;
     const uint16_t* doh = static_cast<const uint16_t*>(p.d_o) + (size_t)h * p.len_q * D;
     const unsigned bytes = (unsigned)p.len_q * D * 2u;
-    Dma::issue(make_rsrc(qh, bytes), q0, sq[buf], wave, lane);
-    Dma::issue(make_rsrc(doh, bytes), q0, sdo[buf], wave, lane);
+    Dma::issue(make_rsrc(qh, bytes), q0, SQ(buf), wave, lane);
+    Dma::issue(make_rsrc(doh, bytes), q0, SDO(buf), wave, lane);
     if (tid < kQT) {
       const int row = q0 + tid;
       const bool ok = row < p.len_q;
@@ -103,8 +111,8 @@ __global__ void __launch_bounds__(kNT, 2) bwd_kv_kernel(BwdParams p) {
     }
   };
   auto store_it = [&](int buf) {
-    if (tid < kQT) slse[buf][tid] = st_lse;
-    else if (!DV && tid < 2 * kQT) sdel[buf][tid - kQT] = st_del;
+    if (tid < kQT) slse[buf * kQT + tid] = st_lse;
+    else if (!DV && tid < 2 * kQT) sdel[buf * kQT + tid - kQT] = st_del;
   };
 
   if (n_it > 0) {
@@ -134,18 +142,18 @@ __global__ void __launch_bounds__(kNT, 2) bwd_kv_kernel(BwdParams p) {
       f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32x32x16(tile_row8<D>(sq[buf], arow, 2 * ks + half), kb[ks], s);
+        s = mfma32x32x16(tile_row8<D>(SQ(buf), arow, 2 * ks + half), kb[ks], s);
         if constexpr (!DV)
-          dp = mfma32x32x16(tile_row8<D>(sdo[buf], arow, 2 * ks + half), vb[ks], dp);
+          dp = mfma32x32x16(tile_row8<D>(SDO(buf), arow, 2 * ks + half), vb[ks], dp);
       }
       u32x4_t pb[2];  // P (dV part) or dS (dK part), bf16
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         // accumulator registers 4*a4 .. 4*a4+3 hold 4 consecutive query rows of the tile
         const int rbase = 32 * b + 16 * (a4 >> 1) + 8 * half + 4 * (a4 & 1);
-        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(&slse[buf][rbase]);
+        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(slse + buf * kQT + rbase);
         f32x4_t d4;
-        if constexpr (!DV) d4 = *reinterpret_cast<const f32x4_t*>(&sdel[buf][rbase]);
+        if constexpr (!DV) d4 = *reinterpret_cast<const f32x4_t*>(sdel + buf * kQT + rbase);
         float v4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -158,7 +166,7 @@ __global__ void __launch_bounds__(kNT, 2) bwd_kv_kernel(BwdParams p) {
         pb[a4 >> 1][2 * (a4 & 1) + 1] = pack_bf16x2(v4[2], v4[3]);
       }
       // dV^T += dO^T P  or  dK^T += Q^T dS (transposed operand via the transpose read)
-      const uint16_t* tt = DV ? sdo[buf] : sq[buf];
+      const uint16_t* tt = DV ? SDO(buf) : SQ(buf);
 #pragma unroll
       for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -186,15 +194,16 @@ __global__ void __launch_bounds__(kNT, 2) bwd_kv_kernel(BwdParams p) {
 }
 
 template <int D>
-__global__ void __launch_bounds__(kNT, 2) bwd_dq_kernel(BwdParams p) {
+__device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int w, char* smem) {
   constexpr int KS = D / 16, NB = D / 32, BM = 32 * kNW;
-  __shared__ __attribute__((aligned(16))) uint16_t sk[2][kKT * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sv[2][kKT * D];
+  uint16_t* const sk_base = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* const sv_base = sk_base + 2 * kKT * D;
+  auto SK = [&](int b) { return sk_base + b * (kKT * D); };
+  auto SV = [&](int b) { return sv_base + b * (kKT * D); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
   const int n_qt = (p.len_q + BM - 1) / BM;
-  const int w = xcd_remap(blockIdx.x, n_qt * p.heads_q);
   const int h_in = w % p.group;
   const int rest = w / p.group;
   const int qt = n_qt - 1 - rest % n_qt;  // causally longest tiles first
@@ -235,8 +244,8 @@ __global__ void __launch_bounds__(kNT, 2) bwd_dq_kernel(BwdParams p) {
   for (int nb = 0; nb < NB; ++nb) dqt[nb] = f32x16_t{};
 
   if (n_kt > 0) {
-    Dma::issue(rk, 0, sk[0], wave, lane);
-    Dma::issue(rv, 0, sv[0], wave, lane);
+    Dma::issue(rk, 0, SK(0), wave, lane);
+    Dma::issue(rv, 0, SV(0), wave, lane);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -248,8 +257,8 @@ __global__ void __launch_bounds__(kNT, 2) bwd_dq_kernel(BwdParams p) {
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < n_kt) {
-      Dma::issue(rk, (kt + 1) * kKT, sk[buf ^ 1], wave, lane);
-      Dma::issue(rv, (kt + 1) * kKT, sv[buf ^ 1], wave, lane);
+      Dma::issue(rk, (kt + 1) * kKT, SK(buf ^ 1), wave, lane);
+      Dma::issue(rv, (kt + 1) * kKT, SV(buf ^ 1), wave, lane);
     }
     const int key0 = kt * kKT;
     const bool wave_visible = !p.causal || key0 - (wave_row0 + 31) <= dpos;
@@ -262,8 +271,8 @@ __global__ void __launch_bounds__(kNT, 2) bwd_dq_kernel(BwdParams p) {
         const int arow = 32 * blk + perm_row(col);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {  // S^T and dP^T chains interleaved
-          s = mfma32x32x16(tile_row8<D>(sk[buf], arow, 2 * ks + half), qb[ks], s);
-          dp = mfma32x32x16(tile_row8<D>(sv[buf], arow, 2 * ks + half), dob[ks], dp);
+          s = mfma32x32x16(tile_row8<D>(SK(buf), arow, 2 * ks + half), qb[ks], s);
+          dp = mfma32x32x16(tile_row8<D>(SV(buf), arow, 2 * ks + half), dob[ks], dp);
         }
         u32x4_t dsb[2];
 #pragma unroll
@@ -286,7 +295,7 @@ __global__ void __launch_bounds__(kNT, 2) bwd_dq_kernel(BwdParams p) {
         for (int q = 0; q < 2; ++q)
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
-            dqt[nb] = mfma32x32x16(tile_col8<D>(sk[buf], 32 * blk + 16 * q, 32 * nb, lane), dsb[q], dqt[nb]);
+            dqt[nb] = mfma32x32x16(tile_col8<D>(SK(buf), 32 * blk + 16 * q, 32 * nb, lane), dsb[q], dqt[nb]);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -307,25 +316,38 @@ __global__ void __launch_bounds__(kNT, 2) bwd_dq_kernel(BwdParams p) {
     }
 }
 
+// One launch per ring step: the dK part's workgroups first (the longest), then the dV part's,
+// then the dQ kernel's, so that the short dQ workgroups fill the tail left by the others. The
+// three bodies share one LDS buffer; n_dk, n_dv, n_dq are the segment sizes (0 = segment off).
+template <int D>
+__global__ void __launch_bounds__(kNT, 2) bwd_kernel(BwdParams p, int n_dk, int n_dv, int n_dq) {
+  constexpr int kSmem = kv_smem_bytes<D>() > dq_smem_bytes<D>() ? kv_smem_bytes<D>()
+                                                                 : dq_smem_bytes<D>();
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
+  int b = blockIdx.x;
+  if (b < n_dk) {
+    bwd_kv_body<D, kPartDK>(p, xcd_remap(b, n_dk), smem);
+    return;
+  }
+  b -= n_dk;
+  if (b < n_dv) {
+    bwd_kv_body<D, kPartDV>(p, xcd_remap(b, n_dv), smem);
+    return;
+  }
+  b -= n_dv;
+  if (b < n_dq) bwd_dq_body<D>(p, xcd_remap(b, n_dq), smem);
+}
+
 template <int D>
 hipError_t launch_d(const BwdParams& p, int which, hipStream_t s) {
-  if (which & 1) {
-    const int n_kt = (p.len_kv + 32 * kNW - 1) / (32 * kNW);
-    hipLaunchKernelGGL((bwd_kv_kernel<D, kPartDV>), dim3((unsigned)(n_kt * p.heads_kv)), dim3(kNT),
-                       0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_kv_kernel<D, kPartDK>), dim3((unsigned)(n_kt * p.heads_kv)), dim3(kNT),
-                       0, s, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (which & 2) {
-    const int n_qt = (p.len_q + 32 * kNW - 1) / (32 * kNW);
-    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(n_qt * p.heads_q)), dim3(kNT), 0, s, p);
-    return hipGetLastError();
-  }
-  return hipSuccess;
+  const int n_kv = ((p.len_kv + 32 * kNW - 1) / (32 * kNW)) * p.heads_kv;
+  const int n_q = ((p.len_q + 32 * kNW - 1) / (32 * kNW)) * p.heads_q;
+  const int n_dk = (which & 1) ? n_kv : 0, n_dv = (which & 1) ? n_kv : 0;
+  const int n_dq = (which & 2) ? n_q : 0;
+  const long long total = (long long)n_dk + n_dv + n_dq;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_kernel<D>), dim3((unsigned)total), dim3(kNT), 0, s, p, n_dk, n_dv, n_dq);
+  return hipGetLastError();
 }
 
 }  // namespace
