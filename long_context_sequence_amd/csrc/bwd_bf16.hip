@@ -130,13 +130,8 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* sme
     const int buf = it & 1;
     if (it + 1 < n_it) load_it(it + 1, buf ^ 1);
     const int q0 = (qt_first + it % per_head) * kQT;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int brow = q0 + 32 * b;  // first row of the block
-      // no row of the block sees the wave's first key: nothing to do
-      if (p.causal && wave_key0 - (brow + 31) > dpos) continue;
-      // some key of the wave invisible to the block's first row: mask
-      const bool need_mask = p.causal && wave_key0 + 31 - brow > dpos;
+    // One 32-row block of the tile against the wave's 32 keys.
+    auto do_block = [&](int b, bool need_mask) {
       const int arow = 32 * b + perm_row(col);
       // S and dP chains interleaved (independent accumulators)
       f32x16_t s = f32x16_t{}, dp = f32x16_t{};
@@ -172,6 +167,21 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* sme
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
           acc[nb] = mfma32x32x16(tile_col8<D>(tt, 32 * b + 16 * q, 32 * nb, lane), pb[q], acc[nb]);
+    };
+    if (!p.causal || wave_key0 + 31 - q0 <= dpos) {
+      // every key of the wave is visible to every row of the tile: both blocks, no branches,
+      // so the scheduler can overlap one block's MFMAs with the other's softmax
+      do_block(0, false);
+      do_block(1, false);
+    } else {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int brow = q0 + 32 * b;  // first row of the block
+        // no row of the block sees the wave's first key: nothing to do
+        if (wave_key0 - (brow + 31) > dpos) continue;
+        // some key of the wave invisible to the block's first row: mask
+        do_block(b, wave_key0 + 31 - brow > dpos);
+      }
     }
     if (it + 1 < n_it) store_it(buf ^ 1);
     __builtin_amdgcn_s_waitcnt(0);
