@@ -51,7 +51,8 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* sme
   auto SDO = [&](int b) { return sdo_base + b * (kQT * D); };
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
+  const int lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int wave = tid >> 6;
   const int n_kt = (p.len_kv + BNK - 1) / BNK;
   const int g = w / n_kt;
   const int kt = w % n_kt;  // ascending: under causality the earliest keys have most work
@@ -96,9 +97,8 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* sme
     const int q0 = (qt_first + it % per_head) * kQT;
     const uint16_t* qh = static_cast<const uint16_t*>(p.q) + (size_t)h * p.len_q * D;
     const uint16_t* doh = static_cast<const uint16_t*>(p.d_o) + (size_t)h * p.len_q * D;
-    const unsigned bytes = (unsigned)p.len_q * D * 2u;
-    Dma::issue(make_rsrc(qh, bytes), q0, SQ(buf), wave, lane);
-    Dma::issue(make_rsrc(doh, bytes), q0, SDO(buf), wave, lane);
+    Dma::issue_lean(qh, q0, p.len_q, SQ(buf), wave, lane);
+    Dma::issue_lean(doh, q0, p.len_q, SDO(buf), wave, lane);
     if (tid < kQT) {
       const int row = q0 + tid;
       const bool ok = row < p.len_q;
@@ -212,7 +212,8 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int w, char* sme
   auto SV = [&](int b) { return sv_base + b * (kKT * D); };
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
+  const int lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int wave = tid >> 6;
   const int n_qt = (p.len_q + BM - 1) / BM;
   const int h_in = w % p.group;
   const int rest = w / p.group;
@@ -246,16 +247,14 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int w, char* sme
   const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (size_t)g * p.len_kv * D;
   const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (size_t)g * p.len_kv * D;
   using Dma = TileDma<D, kKT, kNT>;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg, (unsigned)p.len_kv * D * 2u);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg, (unsigned)p.len_kv * D * 2u);
 
   f32x16_t dqt[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) dqt[nb] = f32x16_t{};
 
   if (n_kt > 0) {
-    Dma::issue(rk, 0, SK(0), wave, lane);
-    Dma::issue(rv, 0, SV(0), wave, lane);
+    Dma::issue(kg, 0, p.len_kv, SK(0), wave, lane);
+    Dma::issue(vg, 0, p.len_kv, SV(0), wave, lane);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -267,8 +266,8 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int w, char* sme
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < n_kt) {
-      Dma::issue(rk, (kt + 1) * kKT, SK(buf ^ 1), wave, lane);
-      Dma::issue(rv, (kt + 1) * kKT, SV(buf ^ 1), wave, lane);
+      Dma::issue(kg, (kt + 1) * kKT, p.len_kv, SK(buf ^ 1), wave, lane);
+      Dma::issue(vg, (kt + 1) * kKT, p.len_kv, SV(buf ^ 1), wave, lane);
     }
     const int key0 = kt * kKT;
     const bool wave_visible = !p.causal || key0 - (wave_row0 + 31) <= dpos;

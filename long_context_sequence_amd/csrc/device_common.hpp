@@ -139,8 +139,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
 // Direct global -> LDS copy of a ROWS x D bf16 tile into the swizzled layout (no registers, no
 // LDS store instructions). One buffer_load_dwordx4 ... lds per wave fills 1 KB of LDS at
 // consecutive 16-byte slots, i.e. 1024 / (2D) whole rows; each lane fetches the source chunk that
-// belongs at its slot. Rows past the end of the buffer read as zeros. Completion is tracked by
-// vmcnt: wait for it before the barrier that publishes the tile.
+// belongs at its slot. The tile's first row goes into the buffer descriptor's base (scalar
+// arithmetic), so the per-lane offsets stay loop-invariant; rows at or past `nrows` read as
+// zeros. Completion is tracked by vmcnt: wait for it before the barrier that publishes the tile.
+// `wave` must be wave-uniform (from readfirstlane) so the LDS base stays scalar.
 template <int D, int ROWS, int NT>
 struct TileDma {
   static constexpr int CH = D / 8;                 // 16-byte chunks per row
@@ -148,8 +150,26 @@ struct TileDma {
   static constexpr int NWAVE = NT / 64;
   static constexpr int ITERS = ROWS / (RPI * NWAVE);
   static_assert(ROWS % (RPI * NWAVE) == 0, "tile must split evenly over the waves");
-  __device__ __forceinline__ static void issue(__amdgpu_buffer_rsrc_t rsrc, int row0,
+  __device__ __forceinline__ static void issue(const uint16_t* src, int row0, int nrows,
                                                uint16_t* lds_tile, int wave, int lane) {
+    const __amdgpu_buffer_rsrc_t rsrc =
+        make_rsrc(src + (size_t)row0 * D, (unsigned)(nrows - row0) * D * 2u);
+#pragma unroll
+    for (int u = 0; u < ITERS; ++u) {
+      const int rbase = (u * NWAVE + wave) * RPI;
+      const int r = rbase + lane / CH;
+      const int c = (lane % CH) ^ tile_swz<D>(r);
+      const unsigned voff = ((unsigned)r * D + 8u * c) * 2u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)(lds_tile + rbase * D), 16, voff, 0, 0, 0);
+    }
+  }
+  // Same copy with the tile's row offset folded into each lane's offset instead of the
+  // descriptor: a few more vector instructions per tile, but no offsets kept live across a loop
+  // (for kernels at the edge of their register budget).
+  __device__ __forceinline__ static void issue_lean(const uint16_t* src, int row0, int nrows,
+                                                    uint16_t* lds_tile, int wave, int lane) {
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(src, (unsigned)nrows * D * 2u);
 #pragma unroll
     for (int u = 0; u < ITERS; ++u) {
       const int rbase = (u * NWAVE + wave) * RPI;

@@ -47,7 +47,8 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(StepParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t sv[2][kBN * D];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
+  const int lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // Work item: (kv head, query tile from the last one down, head within the group). Items of
   // one kv head are contiguous and map to one XCD, so its K/V stay in that XCD's L2; the
@@ -85,8 +86,6 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(StepParams p) {
   const int wave_row0 = q_base + 32 * wave;
 
   using Dma = TileDma<D, kBN, NT>;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg, (unsigned)p.len_kv * D * 2u);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg, (unsigned)p.len_kv * D * 2u);
 
   f32x16_t oacc[NB];
 #pragma unroll
@@ -115,9 +114,9 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(StepParams p) {
   // K_{j+2} (into K_j's buffer) and V_{j+1} (into V_{j-1}'s) are in flight.
   f32x16_t s_cur[SB];
   if (n_kt > 0) {
-    Dma::issue(rk, 0, sk[0], wave, lane);
-    Dma::issue(rv, 0, sv[0], wave, lane);
-    if (n_kt > 1) Dma::issue(rk, kBN, sk[1], wave, lane);
+    Dma::issue(kg, 0, p.len_kv, sk[0], wave, lane);
+    Dma::issue(vg, 0, p.len_kv, sv[0], wave, lane);
+    if (n_kt > 1) Dma::issue(kg, kBN, p.len_kv, sk[1], wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     scores(sk[0], s_cur);
@@ -126,8 +125,8 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(StepParams p) {
 
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < n_kt) Dma::issue(rv, (kt + 1) * kBN, sv[buf ^ 1], wave, lane);
-    if (kt + 2 < n_kt) Dma::issue(rk, (kt + 2) * kBN, sk[buf], wave, lane);
+    if (kt + 1 < n_kt) Dma::issue(vg, (kt + 1) * kBN, p.len_kv, sv[buf ^ 1], wave, lane);
+    if (kt + 2 < n_kt) Dma::issue(kg, (kt + 2) * kBN, p.len_kv, sk[buf], wave, lane);
     const int key0 = kt * kBN;
     // every key of the tile visible to the wave's first row and inside the chunk?
     const bool full = key0 + kBN <= p.len_kv && (!p.causal || key0 + kBN - 1 - wave_row0 <= dpos);
