@@ -213,6 +213,25 @@ cp_status cp_attn_ring_bwd_zigzag(const cp_ring_desc* ring, const void* q, const
                                   const float* lse, float* delta_work, float* dq,
                                   float* dk_chunks, float* dv_chunks, void* stream);
 
+/*
+ * Striped ordering (context-parallelism page, section 5, after Brandon et al.): token t of the
+ * sequence lives on rank t mod n_cp, so rank r holds tokens r, r + n_cp, r + 2 n_cp, ... and
+ * every ring step is a (shifted) triangle of equal work. (The page's wording, "2 n_cp shards,
+ * two per rank in stripes", is taken as garbled: that reading would not balance causal work.)
+ * Within stripe coordinates query i of rank r sees key j of stripe c iff j <= i when c <= r and
+ * j <= i - 1 when c > r, which is the step's causal test with q_pos0 = 0 and kv_pos0 = (c > r).
+ * Layout as for the contiguous ring: q [heads_q, Ls, d] (the rank's stripe, Ls = L / n_cp),
+ * k_chunks/v_chunks [n_cp, heads_kv, Ls, d] (stripe c at index c), o [heads_q, Ls, d], lse
+ * [heads_q, Ls]; ring->chunk_len is Ls.
+ */
+cp_status cp_attn_ring_fwd_striped(const cp_ring_desc* ring, const void* q,
+                                   const void* k_chunks, const void* v_chunks, float* o,
+                                   float* lse, void* stream);
+cp_status cp_attn_ring_bwd_striped(const cp_ring_desc* ring, const void* q,
+                                   const void* k_chunks, const void* v_chunks, const void* d_o,
+                                   const float* o, const float* lse, float* delta_work,
+                                   float* dq, float* dk_chunks, float* dv_chunks, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* cp_attn_status_string(int32_t status);
 

@@ -89,6 +89,11 @@ def load():
     lib.cp_attn_ring_bwd_zigzag.argtypes = [ctypes.POINTER(RingDesc), _P, _P, _P, _P, _P, _P, _P,
                                             _P, _P, _P, _P]
     lib.cp_attn_ring_bwd_zigzag.restype = st
+    lib.cp_attn_ring_fwd_striped.argtypes = [ctypes.POINTER(RingDesc), _P, _P, _P, _P, _P, _P]
+    lib.cp_attn_ring_fwd_striped.restype = st
+    lib.cp_attn_ring_bwd_striped.argtypes = [ctypes.POINTER(RingDesc), _P, _P, _P, _P, _P, _P,
+                                             _P, _P, _P, _P, _P]
+    lib.cp_attn_ring_bwd_striped.restype = st
     lib.cp_attn_status_string.argtypes = [ctypes.c_int32]
     lib.cp_attn_status_string.restype = ctypes.c_char_p
     lib.cp_attn_abi_version.argtypes = []
@@ -329,3 +334,33 @@ def ring_bwd_zigzag(q, k_chunks, v_chunks, d_o, o, lse, delta_work, dq, dk_chunk
                                                  _ptr(delta_work), _ptr(dq), _ptr(dk_chunks),
                                                  _ptr(dv_chunks), _stream()),
                   "cp_attn_ring_bwd_zigzag", allow_skip=False)
+
+
+def ring_fwd_striped(q, k_chunks, v_chunks, o, lse, rank, causal, scale=None):
+    """cp_attn_ring_fwd_striped: token t on rank t mod N_cp; shapes as ring_fwd (stripes)."""
+    _need(q, "q")
+    n_cp, hkv, ls, d = k_chunks.shape
+    _need(k_chunks, "k_chunks", shape=(n_cp, hkv, q.shape[1], q.shape[2]), dtype=q.dtype)
+    _need(v_chunks, "v_chunks", shape=k_chunks.shape, dtype=q.dtype)
+    _need(o, "o", shape=q.shape, dtype=torch.float32)
+    _need(lse, "lse", shape=q.shape[:2], dtype=torch.float32)
+    r = _ring(q, k_chunks, rank, causal, scale)
+    return _check(load().cp_attn_ring_fwd_striped(ctypes.byref(r), _ptr(q), _ptr(k_chunks),
+                                                  _ptr(v_chunks), _ptr(o), _ptr(lse), _stream()),
+                  "cp_attn_ring_fwd_striped", allow_skip=False)
+
+
+def ring_bwd_striped(q, k_chunks, v_chunks, d_o, o, lse, delta_work, dq, dk_chunks, dv_chunks,
+                     rank, causal, scale=None):
+    """cp_attn_ring_bwd_striped; dq, dk_chunks, dv_chunks accumulated."""
+    _bwd_inputs(q, k_chunks[0], v_chunks[0], d_o, lse, delta_work)
+    _need(o, "o", shape=q.shape, dtype=torch.float32)
+    _need(dq, "dq", shape=q.shape, dtype=torch.float32)
+    _need(dk_chunks, "dk_chunks", shape=k_chunks.shape, dtype=torch.float32)
+    _need(dv_chunks, "dv_chunks", shape=k_chunks.shape, dtype=torch.float32)
+    r = _ring(q, k_chunks, rank, causal, scale)
+    return _check(load().cp_attn_ring_bwd_striped(ctypes.byref(r), _ptr(q), _ptr(k_chunks),
+                                                  _ptr(v_chunks), _ptr(d_o), _ptr(o), _ptr(lse),
+                                                  _ptr(delta_work), _ptr(dq), _ptr(dk_chunks),
+                                                  _ptr(dv_chunks), _stream()),
+                  "cp_attn_ring_bwd_striped", allow_skip=False)

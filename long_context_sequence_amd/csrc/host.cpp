@@ -419,4 +419,63 @@ cp_status cp_attn_ring_bwd_zigzag(const cp_ring_desc* ring, const void* q, const
   return CP_OK;
 }
 
+// Striped ordering: stripe-local positions; the step with the chunk after the rank's own
+// (c > rank) sees strictly earlier positions, hence kv_pos0 = 1.
+cp_status cp_attn_ring_fwd_striped(const cp_ring_desc* ring, const void* q,
+                                   const void* k_chunks, const void* v_chunks, float* o,
+                                   float* lse, void* stream) {
+  cp_status st = check_ring(ring);
+  if (st != CP_OK) return st;
+  cp_attn_desc d0 = ring_step_desc(ring, ring->rank, 0);
+  st = check_desc(&d0);
+  if (st != CP_OK) return st;
+  st = check_ptrs({q, k_chunks, v_chunks, o, lse});
+  if (st != CP_OK) return st;
+  const size_t chunk = (size_t)ring->heads_kv * ring->chunk_len * ring->head_dim;
+  const size_t esz = elem_size(ring->dtype);
+  bool started = false;
+  for (int32_t s = 0; s < ring->n_cp; ++s) {
+    const int32_t c = ((ring->rank - s) % ring->n_cp + ring->n_cp) % ring->n_cp;
+    cp_attn_desc d = d0;
+    d.q_pos0 = 0;
+    d.kv_pos0 = (ring->causal && c > ring->rank) ? 1 : 0;
+    d.accumulate = started ? 1 : 0;
+    st = cp_attn_step(&d, q, static_cast<const char*>(k_chunks) + c * chunk * esz,
+                      static_cast<const char*>(v_chunks) + c * chunk * esz, o, lse, stream);
+    if (st != CP_OK && st != CP_STEP_SKIPPED) return st;
+    if (st == CP_OK) started = true;
+  }
+  return CP_OK;
+}
+
+cp_status cp_attn_ring_bwd_striped(const cp_ring_desc* ring, const void* q,
+                                   const void* k_chunks, const void* v_chunks, const void* d_o,
+                                   const float* o, const float* lse, float* delta_work,
+                                   float* dq, float* dk_chunks, float* dv_chunks, void* stream) {
+  cp_status st = check_ring(ring);
+  if (st != CP_OK) return st;
+  cp_attn_desc d0 = ring_step_desc(ring, ring->rank, 0);
+  st = check_desc(&d0);
+  if (st != CP_OK) return st;
+  if (ring->dtype != CP_BF16) return CP_ERR_UNSUPPORTED;
+  st = check_ptrs({q, k_chunks, v_chunks, d_o, o, lse, delta_work, dq, dk_chunks, dv_chunks});
+  if (st != CP_OK) return st;
+  const int64_t rows = (int64_t)ring->heads_q * ring->chunk_len;
+  st = cp_attn_bwd_prep(rows, ring->head_dim, ring->dtype, o, d_o, delta_work, stream);
+  if (st != CP_OK) return st;
+  const size_t chunk = (size_t)ring->heads_kv * ring->chunk_len * ring->head_dim;
+  const size_t esz = elem_size(ring->dtype);
+  for (int32_t s = 0; s < ring->n_cp; ++s) {
+    const int32_t c = ((ring->rank - s) % ring->n_cp + ring->n_cp) % ring->n_cp;
+    cp_attn_desc d = d0;
+    d.q_pos0 = 0;
+    d.kv_pos0 = (ring->causal && c > ring->rank) ? 1 : 0;
+    st = cp_attn_bwd(&d, q, static_cast<const char*>(k_chunks) + c * chunk * esz,
+                     static_cast<const char*>(v_chunks) + c * chunk * esz, d_o, lse, delta_work,
+                     dq, dk_chunks + c * chunk, dv_chunks + c * chunk, stream);
+    if (st != CP_OK && st != CP_STEP_SKIPPED) return st;
+  }
+  return CP_OK;
+}
+
 }  // extern "C"
