@@ -27,6 +27,57 @@ constexpr int kKT = 64;    // keys per tile (dq)
 constexpr int kNW = 4;     // waves per workgroup
 constexpr int kNT = 64 * kNW;
 
+// Instruction-scheduling strategy handed to the compiler for the unmasked tile bodies of the
+// kv parts and the dQ part (an iglp_opt strategy number; negative = compiler default).
+#ifndef CP_BWD_IGLP_KV
+#define CP_BWD_IGLP_KV -1
+#endif
+#ifndef CP_BWD_IGLP_DQ
+#define CP_BWD_IGLP_DQ -1
+#endif
+// LDS operand reads issued ahead of their MFMA in the S/dP chains of the kv parts and of the
+// dQ part (0 = compiler's choice). Measured at the 208K shard: the dQ part gains ~7% at 2, the
+// kv parts lose ~5% at any depth.
+#ifndef CP_BWD_PF_KV
+#define CP_BWD_PF_KV 0
+#endif
+#ifndef CP_BWD_PF_DQ
+#define CP_BWD_PF_DQ 2
+#endif
+
+// Two MFMA chains acc_a += A_a[ks] * B_a[ks], acc_b += A_b[ks] * B_b[ks] over ks, with the A
+// operands read from LDS PF steps ahead of their use (the reads of step ks + PF are issued
+// before the MFMAs of step ks, and scheduling fences keep them there), so the LDS latency
+// overlaps the matrix work. With PF = 0 the compiler schedules freely.
+template <int KS, int PF, bool TWO, typename LA, typename LB>
+__device__ __forceinline__ void mfma_chains(LA load_a, LB load_b, const u32x4_t* ba,
+                                            const u32x4_t* bb, f32x16_t& acc_a, f32x16_t& acc_b) {
+  if constexpr (PF == 0) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      acc_a = mfma32x32x16(load_a(ks), ba[ks], acc_a);
+      if constexpr (TWO) acc_b = mfma32x32x16(load_b(ks), bb[ks], acc_b);
+    }
+  } else {
+    u32x4_t ra[KS], rb[KS];
+#pragma unroll
+    for (int ks = 0; ks < PF; ++ks) {
+      ra[ks] = load_a(ks);
+      if constexpr (TWO) rb[ks] = load_b(ks);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + PF < KS) {
+        ra[ks + PF] = load_a(ks + PF);
+        if constexpr (TWO) rb[ks + PF] = load_b(ks + PF);
+      }
+      acc_a = mfma32x32x16(ra[ks], ba[ks], acc_a);
+      if constexpr (TWO) acc_b = mfma32x32x16(rb[ks], bb[ks], acc_b);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 // PART selects the products: kPartDV = S, P, dV^T += dO^T P (K operand only, LSE only);
 // kPartDK = S, dP, dS, dK^T += Q^T dS (K and V operands, LSE and delta). Splitting dV from dK
 // recomputes S once more but halves the accumulators, so each kernel runs two waves per SIMD.
@@ -135,12 +186,9 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* sme
       const int arow = 32 * b + perm_row(col);
       // S and dP chains interleaved (independent accumulators)
       f32x16_t s = f32x16_t{}, dp = f32x16_t{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32x32x16(tile_row8<D>(SQ(buf), arow, 2 * ks + half), kb[ks], s);
-        if constexpr (!DV)
-          dp = mfma32x32x16(tile_row8<D>(SDO(buf), arow, 2 * ks + half), vb[ks], dp);
-      }
+      mfma_chains<KS, CP_BWD_PF_KV, !DV>(
+          [&](int ks) { return tile_row8<D>(SQ(buf), arow, 2 * ks + half); },
+          [&](int ks) { return tile_row8<D>(SDO(buf), arow, 2 * ks + half); }, kb, vb, s, dp);
       u32x4_t pb[2];  // P (dV part) or dS (dK part), bf16
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
@@ -171,6 +219,7 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* sme
     if (!p.causal || wave_key0 + 31 - q0 <= dpos) {
       // every key of the wave is visible to every row of the tile: both blocks, no branches,
       // so the scheduler can overlap one block's MFMAs with the other's softmax
+      if constexpr (CP_BWD_IGLP_KV >= 0) __builtin_amdgcn_iglp_opt(CP_BWD_IGLP_KV < 0 ? 0 : CP_BWD_IGLP_KV);
       do_block(0, false);
       do_block(1, false);
     } else {
@@ -270,42 +319,46 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int w, char* sme
       Dma::issue(vg, (kt + 1) * kKT, p.len_kv, SV(buf ^ 1), wave, lane);
     }
     const int key0 = kt * kKT;
-    const bool wave_visible = !p.causal || key0 - (wave_row0 + 31) <= dpos;
-    if (wave_visible) {
-      const bool need_mask =
-          key0 + kKT > p.len_kv || (p.causal && key0 + kKT - 1 - wave_row0 > dpos);
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        f32x16_t s = f32x16_t{}, dp = f32x16_t{};
-        const int arow = 32 * blk + perm_row(col);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {  // S^T and dP^T chains interleaved
-          s = mfma32x32x16(tile_row8<D>(SK(buf), arow, 2 * ks + half), qb[ks], s);
-          dp = mfma32x32x16(tile_row8<D>(SV(buf), arow, 2 * ks + half), dob[ks], dp);
-        }
-        u32x4_t dsb[2];
-#pragma unroll
-        for (int r2 = 0; r2 < 8; ++r2) {
-          float dsv[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int r = 2 * r2 + e;
-            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -lse2));
-            if (need_mask) {
-              const int kk = key0 + 32 * blk + perm_row(8 * (r >> 2) + 4 * half + (r & 3));
-              const bool vis = (kk < p.len_kv) & ((!p.causal) | (kk - qi <= dpos));
-              pr = vis ? pr : 0.f;
-            }
-            dsv[e] = pr * (dp[r] - del);
-          }
-          dsb[r2 >> 2][r2 & 3] = pack_bf16x2(dsv[0], dsv[1]);
-        }
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            dqt[nb] = mfma32x32x16(tile_col8<D>(SK(buf), 32 * blk + 16 * q, 32 * nb, lane), dsb[q], dqt[nb]);
+    // One 32-key block of the tile against the wave's 32 query rows.
+    auto do_block = [&](int blk, bool need_mask) {
+      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+      const int arow = 32 * blk + perm_row(col);
+      mfma_chains<KS, CP_BWD_PF_DQ, true>(  // S^T and dP^T chains interleaved
+          [&](int ks) { return tile_row8<D>(SK(buf), arow, 2 * ks + half); },
+          [&](int ks) { return tile_row8<D>(SV(buf), arow, 2 * ks + half); }, qb, dob, s, dp);
+      // Accumulator register r holds key key0 + 32 blk + 8 half + koff(r) (rows loaded through
+      // perm_row), with koff(r) = (r & 7) + 16 (r >> 3); it is visible iff koff(r) <= klim.
+      int klim = 0;
+      if (need_mask) {
+        const int kb0 = key0 + 32 * blk + 8 * half;
+        klim = p.len_kv - 1 - kb0;
+        if (p.causal) klim = min(klim, qi + dpos - kb0);
       }
+      u32x4_t dsb[2];
+#pragma unroll
+      for (int r2 = 0; r2 < 8; ++r2) {
+        float dsv[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = 2 * r2 + e;
+          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -lse2));
+          if (need_mask && (r & 7) + 16 * (r >> 3) > klim) pr = 0.f;
+          dsv[e] = pr * (dp[r] - del);
+        }
+        dsb[r2 >> 2][r2 & 3] = pack_bf16x2(dsv[0], dsv[1]);
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          dqt[nb] = mfma32x32x16(tile_col8<D>(SK(buf), 32 * blk + 16 * q, 32 * nb, lane), dsb[q], dqt[nb]);
+    };
+    const bool need_mask =
+        key0 + kKT > p.len_kv || (p.causal && key0 + kKT - 1 - wave_row0 > dpos);
+    if (!p.causal || key0 - (wave_row0 + 31) <= dpos) {
+      if constexpr (CP_BWD_IGLP_DQ >= 0) __builtin_amdgcn_iglp_opt(CP_BWD_IGLP_DQ < 0 ? 0 : CP_BWD_IGLP_DQ);
+      do_block(0, need_mask);
+      do_block(1, need_mask);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
