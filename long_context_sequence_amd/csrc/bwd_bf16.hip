@@ -141,35 +141,35 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* sme
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16_t{};
 
   using Dma = TileDma<D, kQT, kNT>;
-  float st_lse = 0.f, st_del = 0.f;
-  // Issue the direct loads of tile `it` into LDS buffer `buf`; fetch its LSE/delta to registers.
-  auto load_it = [&](int it, int buf) {
+  // Issue the direct loads of tile `it` into LDS buffer `buf` and return this thread's staging
+  // value for it: thread t < kQT fetches the LSE of row t (-inf past the end), thread kQT + t
+  // (dK part) delta of row t. One value per thread, returned rather than written through a
+  // capture, so that it stays in a register.
+  auto load_it = [&](int it, int buf) -> float {
     const int h = g * p.group + it / per_head;
     const int q0 = (qt_first + it % per_head) * kQT;
     const uint16_t* qh = static_cast<const uint16_t*>(p.q) + (size_t)h * p.len_q * D;
     const uint16_t* doh = static_cast<const uint16_t*>(p.d_o) + (size_t)h * p.len_q * D;
     Dma::issue_lean(qh, q0, p.len_q, SQ(buf), wave, lane);
     Dma::issue_lean(doh, q0, p.len_q, SDO(buf), wave, lane);
-    if (tid < kQT) {
-      const int row = q0 + tid;
-      const bool ok = row < p.len_q;
-      const float l = ok ? p.lse[(size_t)h * p.len_q + row] : -INFINITY;
-      // rows past the end or with no visible key anywhere get P = 0
-      st_lse = l == -INFINITY ? INFINITY : l * kLog2e;
-    } else if (!DV && tid < 2 * kQT) {
-      const int row = q0 + tid - kQT;
-      st_del = row < p.len_q ? p.delta[(size_t)h * p.len_q + row] : 0.f;
+    const bool is_lse = tid < kQT;
+    const int row = q0 + (is_lse ? tid : tid - kQT);
+    float v = is_lse ? -INFINITY : 0.f;
+    if (row < p.len_q && (is_lse || (!DV && tid < 2 * kQT))) {
+      const float* src = is_lse ? p.lse : p.delta;
+      v = src[(size_t)h * p.len_q + row];
     }
+    return v;
   };
-  auto store_it = [&](int buf) {
-    if (tid < kQT) slse[buf * kQT + tid] = st_lse;
-    else if (!DV && tid < 2 * kQT) sdel[buf * kQT + tid - kQT] = st_del;
+  // Publish a staged value; the LSE conversion happens here, after the tile's compute, so the
+  // wait for the load is not paid up front. Rows past the end or with no visible key anywhere
+  // get lse2 = +inf, hence P = 0.
+  auto store_it = [&](int buf, float v) {
+    if (tid < kQT) slse[buf * kQT + tid] = v == -INFINITY ? INFINITY : v * kLog2e;
+    else if (!DV && tid < 2 * kQT) sdel[buf * kQT + tid - kQT] = v;
   };
 
-  if (n_it > 0) {
-    load_it(0, 0);
-    store_it(0);
-  }
+  if (n_it > 0) store_it(0, load_it(0, 0));
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -179,7 +179,8 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* sme
 
   for (int it = 0; it < n_it; ++it) {
     const int buf = it & 1;
-    if (it + 1 < n_it) load_it(it + 1, buf ^ 1);
+    float stg = 0.f;
+    if (it + 1 < n_it) stg = load_it(it + 1, buf ^ 1);
     const int q0 = (qt_first + it % per_head) * kQT;
     // One 32-row block of the tile against the wave's 32 keys.
     auto do_block = [&](int b, bool need_mask) {
@@ -232,7 +233,7 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* sme
         do_block(b, wave_key0 + 31 - brow > dpos);
       }
     }
-    if (it + 1 < n_it) store_it(buf ^ 1);
+    if (it + 1 < n_it) store_it(buf ^ 1, stg);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }

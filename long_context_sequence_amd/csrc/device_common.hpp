@@ -136,6 +136,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
                                            0x00020000);
 }
 
+// One direct global -> LDS load: 16 bytes per lane from `rsrc` at byte offset `voff` into the
+// LDS block starting at `lds` (lane i's bytes land at lds + 16 i). Issued as an explicit
+// instruction rather than through the compiler's builtin, which makes every later LDS read that
+// the compiler cannot prove disjoint from the destination wait for the load (vmcnt), and would
+// so serialise a double-buffered pipeline on its own prefetch. The caller is responsible for
+// completion: s_waitcnt vmcnt(0) and a workgroup barrier before anything reads the block.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, unsigned voff,
+                                          const void* lds) {
+  const unsigned base = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(__attribute__((address_space(3))) const void*)lds);
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(base)
+               : "memory", "m0");
+}
+
 // Direct global -> LDS copy of a ROWS x D bf16 tile into the swizzled layout (no registers, no
 // LDS store instructions). One buffer_load_dwordx4 ... lds per wave fills 1 KB of LDS at
 // consecutive 16-byte slots, i.e. 1024 / (2D) whole rows; each lane fetches the source chunk that
@@ -160,8 +176,7 @@ struct TileDma {
       const int r = rbase + lane / CH;
       const int c = (lane % CH) ^ tile_swz<D>(r);
       const unsigned voff = ((unsigned)r * D + 8u * c) * 2u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (__attribute__((address_space(3))) void*)(lds_tile + rbase * D), 16, voff, 0, 0, 0);
+      lds_dma16(rsrc, voff, lds_tile + rbase * D);
     }
   }
   // Same copy with the tile's row offset folded into each lane's offset instead of the
@@ -176,8 +191,7 @@ struct TileDma {
       const int r = rbase + lane / CH;
       const int c = (lane % CH) ^ tile_swz<D>(r);
       const unsigned voff = ((unsigned)(row0 + r) * D + 8u * c) * 2u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (__attribute__((address_space(3))) void*)(lds_tile + rbase * D), 16, voff, 0, 0, 0);
+      lds_dma16(rsrc, voff, lds_tile + rbase * D);
     }
   }
 };

@@ -43,8 +43,11 @@ template <int D, int NW, int kBN>
 __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(StepParams p) {
   constexpr int NT = NW * 64, BM = 32 * NW, KS = D / 16, NB = D / 32;
   constexpr int SB = kBN / 32;  // 32-key blocks per tile
-  __shared__ __attribute__((aligned(16))) uint16_t sk[2][kBN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sv[2][kBN * D];
+  // LDS: region r holds K tile slot r followed by V tile slot 1 - r, so that the tiles one
+  // iteration fills (K_{j+2}, V_{j+1}) form one region and the tiles it reads (K_{j+1}, V_j)
+  // the other.
+  constexpr int kTile = kBN * D;
+  __shared__ __attribute__((aligned(16))) uint16_t sreg[2][2 * kTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, half = lane >> 5, col = lane & 31;
@@ -114,19 +117,26 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(StepParams p) {
   // K_{j+2} (into K_j's buffer) and V_{j+1} (into V_{j-1}'s) are in flight.
   f32x16_t s_cur[SB];
   if (n_kt > 0) {
-    Dma::issue(kg, 0, p.len_kv, sk[0], wave, lane);
-    Dma::issue(vg, 0, p.len_kv, sv[0], wave, lane);
-    if (n_kt > 1) Dma::issue(kg, kBN, p.len_kv, sk[1], wave, lane);
+    Dma::issue(kg, 0, p.len_kv, sreg[0], wave, lane);           // K_0: K slot 0
+    Dma::issue(vg, 0, p.len_kv, sreg[1] + kTile, wave, lane);   // V_0: V slot 0
+    if (n_kt > 1) Dma::issue(kg, kBN, p.len_kv, sreg[1], wave, lane);  // K_1: K slot 1
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    scores(sk[0], s_cur);
+    scores(sreg[0], s_cur);
     __syncthreads();  // every wave is done with K_0 before K_2 lands in its buffer
   }
 
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_kt) Dma::issue(vg, (kt + 1) * kBN, p.len_kv, sv[buf ^ 1], wave, lane);
-    if (kt + 2 < n_kt) Dma::issue(kg, (kt + 2) * kBN, p.len_kv, sk[buf], wave, lane);
+  // One iteration. The region it fills by direct loads (wr: K_{j+2} into K slot j%2, V_{j+1}
+  // into V slot (j+1)%2) and the region it reads (rd: K_{j+1}, V_j) are passed as restrict
+  // pointers; knowing they are disjoint, the compiler does not make the LDS reads of V_j wait
+  // for the loads in flight.
+  auto iteration = [&](int kt, uint16_t* __restrict__ wr, const uint16_t* __restrict__ rd) {
+    uint16_t* const k_wr = wr;
+    uint16_t* const v_wr = wr + kTile;
+    const uint16_t* const k_rd = rd;
+    const uint16_t* const v_rd = rd + kTile;
+    if (kt + 1 < n_kt) Dma::issue(vg, (kt + 1) * kBN, p.len_kv, v_wr, wave, lane);
+    if (kt + 2 < n_kt) Dma::issue(kg, (kt + 2) * kBN, p.len_kv, k_wr, wave, lane);
     const int key0 = kt * kBN;
     // every key of the tile visible to the wave's first row and inside the chunk?
     const bool full = key0 + kBN <= p.len_kv && (!p.causal || key0 + kBN - 1 - wave_row0 <= dpos);
@@ -163,7 +173,7 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(StepParams p) {
     // shares a basic block with the exp work below; on the last tile it reads the other (stale
     // but in-bounds) K buffer and the result is discarded.
     f32x16_t s_nxt[SB];
-    scores(sk[buf ^ 1], s_nxt);
+    scores(k_rd, s_nxt);
 
     // ... while P_j = exp2(S_j*c2 - m) goes to bf16 (PV operand); the row sum stays fp32.
     u32x4_t pb[2 * SB];
@@ -186,10 +196,14 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(StepParams p) {
     for (int kk = 0; kk < 2 * SB; ++kk)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        oacc[nb] = mfma32x32x16(tile_col8<D>(sv[buf], 16 * kk, 32 * nb, lane), pb[kk], oacc[nb]);
+        oacc[nb] = mfma32x32x16(tile_col8<D>(v_rd, 16 * kk, 32 * nb, lane), pb[kk], oacc[nb]);
 
 #pragma unroll
     for (int blk = 0; blk < SB; ++blk) s_cur[blk] = s_nxt[blk];
+  };
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int buf = kt & 1;
+    iteration(kt, sreg[buf], sreg[buf ^ 1]);
     // V_{j+1} and K_{j+2} have landed and every wave is done with V_j and K_{j+1}
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
