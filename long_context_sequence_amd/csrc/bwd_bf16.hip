@@ -39,7 +39,11 @@ constexpr int kNT = 64 * kNW;
 // dQ part (0 = compiler's choice). Measured at the 208K shard: the dQ part gains ~7% at 2, the
 // kv parts lose ~5% at any depth.
 #ifndef CP_BWD_PF_KV
-#define CP_BWD_PF_KV 0
+#define CP_BWD_PF_KV 2
+#endif
+// The same for the transposed operands of the dK/dV/dQ accumulation products.
+#ifndef CP_BWD_PF_ACC
+#define CP_BWD_PF_ACC 0
 #endif
 #ifndef CP_BWD_PF_DQ
 #define CP_BWD_PF_DQ 2
@@ -73,6 +77,26 @@ __device__ __forceinline__ void mfma_chains(LA load_a, LB load_b, const u32x4_t*
       }
       acc_a = mfma32x32x16(ra[ks], ba[ks], acc_a);
       if constexpr (TWO) acc_b = mfma32x32x16(rb[ks], bb[ks], acc_b);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// N MFMAs step(i, A_i) whose A operands are LDS reads load(i), issued PF steps ahead of their
+// use behind scheduling fences (PF = 0: compiler's schedule).
+template <int N, int PF, typename LA, typename ST>
+__device__ __forceinline__ void mfma_pipe(LA load, ST step) {
+  if constexpr (PF == 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) step(i, load(i));
+  } else {
+    u32x4_t ra[N];
+#pragma unroll
+    for (int i = 0; i < PF && i < N; ++i) ra[i] = load(i);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if (i + PF < N) ra[i + PF] = load(i + PF);
+      step(i, ra[i]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -211,11 +235,9 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* sme
       }
       // dV^T += dO^T P  or  dK^T += Q^T dS (transposed operand via the transpose read)
       const uint16_t* tt = DV ? SDO(buf) : SQ(buf);
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          acc[nb] = mfma32x32x16(tile_col8<D>(tt, 32 * b + 16 * q, 32 * nb, lane), pb[q], acc[nb]);
+      mfma_pipe<2 * NB, CP_BWD_PF_ACC>(
+          [&](int i) { return tile_col8<D>(tt, 32 * b + 16 * (i / NB), 32 * (i % NB), lane); },
+          [&](int i, const u32x4_t& a) { acc[i % NB] = mfma32x32x16(a, pb[i / NB], acc[i % NB]); });
     };
     if (!p.causal || wave_key0 + 31 - q0 <= dpos) {
       // every key of the wave is visible to every row of the tile: both blocks, no branches,
@@ -348,11 +370,9 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int w, char* sme
         }
         dsb[r2 >> 2][r2 & 3] = pack_bf16x2(dsv[0], dsv[1]);
       }
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          dqt[nb] = mfma32x32x16(tile_col8<D>(SK(buf), 32 * blk + 16 * q, 32 * nb, lane), dsb[q], dqt[nb]);
+      mfma_pipe<2 * NB, CP_BWD_PF_ACC>(
+          [&](int i) { return tile_col8<D>(SK(buf), 32 * blk + 16 * (i / NB), 32 * (i % NB), lane); },
+          [&](int i, const u32x4_t& a) { dqt[i % NB] = mfma32x32x16(a, dsb[i / NB], dqt[i % NB]); });
     };
     const bool need_mask =
         key0 + kKT > p.len_kv || (p.causal && key0 + kKT - 1 - wave_row0 > dpos);
