@@ -27,14 +27,6 @@ constexpr int kKT = 64;    // keys per tile (dq)
 constexpr int kNW = 4;     // waves per workgroup
 constexpr int kNT = 64 * kNW;
 
-// Instruction-scheduling strategy handed to the compiler for the unmasked tile bodies of the
-// kv parts and the dQ part (an iglp_opt strategy number; negative = compiler default).
-#ifndef CP_BWD_IGLP_KV
-#define CP_BWD_IGLP_KV -1
-#endif
-#ifndef CP_BWD_IGLP_DQ
-#define CP_BWD_IGLP_DQ -1
-#endif
 // LDS operand reads issued ahead of their MFMA in the S/dP chains of the kv parts and of the
 // dQ part (0 = compiler's choice). Measured at the 208K shard: the dQ part gains ~7% at 2, the
 // kv parts lose ~5% at any depth.
@@ -189,8 +181,9 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* sme
   // wait for the load is not paid up front. Rows past the end or with no visible key anywhere
   // get lse2 = +inf, hence P = 0.
   auto store_it = [&](int buf, float v) {
-    if (tid < kQT) slse[buf * kQT + tid] = v == -INFINITY ? INFINITY : v * kLog2e;
-    else if (!DV && tid < 2 * kQT) sdel[buf * kQT + tid - kQT] = v;
+    const float l2 = v == -INFINITY ? INFINITY : v * kLog2e;
+    if (tid < kQT) slse[buf * kQT + tid] = l2;
+    else if (!DV && tid < 2 * kQT) sdel[buf * kQT + tid - kQT] = -v;  // dP starts at -delta
   };
 
   if (n_it > 0) store_it(0, load_it(0, 0));
@@ -206,43 +199,62 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* sme
     float stg = 0.f;
     if (it + 1 < n_it) stg = load_it(it + 1, buf ^ 1);
     const int q0 = (qt_first + it % per_head) * kQT;
-    // One 32-row block of the tile against the wave's 32 keys.
-    auto do_block = [&](int b, bool need_mask) {
+    // One 32-row block of the tile against the wave's 32 keys, in three steps:
+    // chains: S = Q K^T (and dP = dO V^T) on the matrix cores;
+    auto chains = [&](int b, f32x16_t& s, f32x16_t& dp, auto pf) {
       const int arow = 32 * b + perm_row(col);
-      // S and dP chains interleaved (independent accumulators)
-      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
-      mfma_chains<KS, CP_BWD_PF_KV, !DV>(
+      s = f32x16_t{};
+      dp = f32x16_t{};
+      if constexpr (!DV) {
+        // dP accumulates onto -delta of its rows, so that dS = P * dP needs no subtraction
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int rbase = 32 * b + 16 * (a4 >> 1) + 8 * half + 4 * (a4 & 1);
+          const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(sdel + buf * kQT + rbase);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dp[4 * a4 + e] = d4[e];
+        }
+      }
+      mfma_chains<KS, decltype(pf)::value, !DV>(
           [&](int ks) { return tile_row8<D>(SQ(buf), arow, 2 * ks + half); },
           [&](int ks) { return tile_row8<D>(SDO(buf), arow, 2 * ks + half); }, kb, vb, s, dp);
-      u32x4_t pb[2];  // P (dV part) or dS (dK part), bf16
+    };
+    // soft: P = exp2(S*c - lse2) (dV part) or dS = P (dP - delta) (dK part), to bf16;
+    auto soft = [&](int b, const f32x16_t& s, const f32x16_t& dp, bool need_mask,
+                    u32x4_t (&pb)[2]) {
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         // accumulator registers 4*a4 .. 4*a4+3 hold 4 consecutive query rows of the tile
         const int rbase = 32 * b + 16 * (a4 >> 1) + 8 * half + 4 * (a4 & 1);
-        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(slse + buf * kQT + rbase);
-        f32x4_t d4;
-        if constexpr (!DV) d4 = *reinterpret_cast<const f32x4_t*>(sdel + buf * kQT + rbase);
         float v4[4];
+        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(slse + buf * kQT + rbase);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * a4 + e], c2, -l4[e]));
           if (need_mask && key - (q0 + rbase + e) > dpos) pr = 0.f;
           if constexpr (DV) v4[e] = pr;
-          else v4[e] = pr * (dp[4 * a4 + e] - d4[e]);
+          else v4[e] = pr * dp[4 * a4 + e];  // P (dP - delta)
         }
         pb[a4 >> 1][2 * (a4 & 1)] = pack_bf16x2(v4[0], v4[1]);
         pb[a4 >> 1][2 * (a4 & 1) + 1] = pack_bf16x2(v4[2], v4[3]);
       }
-      // dV^T += dO^T P  or  dK^T += Q^T dS (transposed operand via the transpose read)
+    };
+    // accum: dV^T += dO^T P or dK^T += Q^T dS (transposed operand via the transpose read).
+    auto accum = [&](int b, const u32x4_t (&pb)[2]) {
       const uint16_t* tt = DV ? SDO(buf) : SQ(buf);
       mfma_pipe<2 * NB, CP_BWD_PF_ACC>(
           [&](int i) { return tile_col8<D>(tt, 32 * b + 16 * (i / NB), 32 * (i % NB), lane); },
           [&](int i, const u32x4_t& a) { acc[i % NB] = mfma32x32x16(a, pb[i / NB], acc[i % NB]); });
     };
+    auto do_block = [&](int b, bool need_mask) {
+      f32x16_t s, dp;
+      u32x4_t pb[2];
+      chains(b, s, dp, std::integral_constant<int, CP_BWD_PF_KV>{});
+      soft(b, s, dp, need_mask, pb);
+      accum(b, pb);
+    };
     if (!p.causal || wave_key0 + 31 - q0 <= dpos) {
-      // every key of the wave is visible to every row of the tile: both blocks, no branches,
-      // so the scheduler can overlap one block's MFMAs with the other's softmax
-      if constexpr (CP_BWD_IGLP_KV >= 0) __builtin_amdgcn_iglp_opt(CP_BWD_IGLP_KV < 0 ? 0 : CP_BWD_IGLP_KV);
+      // every key of the wave is visible to every row of the tile: no mask, no branches
       do_block(0, false);
       do_block(1, false);
     } else {
@@ -377,7 +389,6 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int w, char* sme
     const bool need_mask =
         key0 + kKT > p.len_kv || (p.causal && key0 + kKT - 1 - wave_row0 > dpos);
     if (!p.causal || key0 - (wave_row0 + 31) <= dpos) {
-      if constexpr (CP_BWD_IGLP_DQ >= 0) __builtin_amdgcn_iglp_opt(CP_BWD_IGLP_DQ < 0 ? 0 : CP_BWD_IGLP_DQ);
       do_block(0, need_mask);
       do_block(1, need_mask);
     }

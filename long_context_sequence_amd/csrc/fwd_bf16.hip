@@ -115,14 +115,14 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(StepParams p) {
   // S_j (computed in iteration j-1) and, while the VALU turns S_j into P_j, the matrix cores
   // compute S_{j+1}; then O += V_j^T P_j. LDS: K_{j+1} and V_j are resident; the direct loads of
   // K_{j+2} (into K_j's buffer) and V_{j+1} (into V_{j-1}'s) are in flight.
-  f32x16_t s_cur[SB];
+  f32x16_t s_a[SB], s_b[SB];  // S of the current tile and of the next one, alternating
   if (n_kt > 0) {
     Dma::issue(kg, 0, p.len_kv, sreg[0], wave, lane);           // K_0: K slot 0
     Dma::issue(vg, 0, p.len_kv, sreg[1] + kTile, wave, lane);   // V_0: V slot 0
     if (n_kt > 1) Dma::issue(kg, kBN, p.len_kv, sreg[1], wave, lane);  // K_1: K slot 1
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    scores(sreg[0], s_cur);
+    scores(sreg[0], s_a);
     __syncthreads();  // every wave is done with K_0 before K_2 lands in its buffer
   }
 
@@ -130,7 +130,8 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(StepParams p) {
   // into V slot (j+1)%2) and the region it reads (rd: K_{j+1}, V_j) are passed as restrict
   // pointers; knowing they are disjoint, the compiler does not make the LDS reads of V_j wait
   // for the loads in flight.
-  auto iteration = [&](int kt, uint16_t* __restrict__ wr, const uint16_t* __restrict__ rd) {
+  auto iteration = [&](int kt, uint16_t* __restrict__ wr, const uint16_t* __restrict__ rd,
+                       f32x16_t (&s_cur)[SB], f32x16_t (&s_nxt)[SB]) {
     uint16_t* const k_wr = wr;
     uint16_t* const v_wr = wr + kTile;
     const uint16_t* const k_rd = rd;
@@ -172,7 +173,6 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(StepParams p) {
     // S_{j+1} on the matrix cores (independent of what follows) ... Unconditional so that it
     // shares a basic block with the exp work below; on the last tile it reads the other (stale
     // but in-bounds) K buffer and the result is discarded.
-    f32x16_t s_nxt[SB];
     scores(k_rd, s_nxt);
 
     // ... while P_j = exp2(S_j*c2 - m) goes to bf16 (PV operand); the row sum stays fp32.
@@ -198,15 +198,18 @@ __global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(StepParams p) {
       for (int nb = 0; nb < NB; ++nb)
         oacc[nb] = mfma32x32x16(tile_col8<D>(v_rd, 16 * kk, 32 * nb, lane), pb[kk], oacc[nb]);
 
-#pragma unroll
-    for (int blk = 0; blk < SB; ++blk) s_cur[blk] = s_nxt[blk];
   };
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    iteration(kt, sreg[buf], sreg[buf ^ 1]);
+  // Unrolled by two so that the buffers and the S registers swap roles without copies.
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    iteration(kt, sreg[0], sreg[1], s_a, s_b);
     // V_{j+1} and K_{j+2} have landed and every wave is done with V_j and K_{j+1}
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (kt + 1 < n_kt) {
+      iteration(kt + 1, sreg[1], sreg[0], s_b, s_a);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
   }
 
   // Epilogue: O = O^T / l, LSE = ln(sum exp(s)) = (m + log2 l) * ln 2.
