@@ -3,7 +3,8 @@
 This module holds no attention arithmetic. It draws N(0, 1) tensors with numpy's PCG64,
 optionally RMS-normalises each length-d row, and rounds to bfloat16 with round-to-nearest-even.
 
-Seeding: ``SeedSequence([workload_key, tensor_id, index])`` with tensor ids q=1, k=2, v=3, do=4.
+Seeding: ``SeedSequence([workload_key, tensor_id, index])`` with tensor ids q=1, k=2, v=3, do=4
+(attention) and x=5, h=6 (convolution: the signal shards and the filter bank).
 ``index`` is the rank for the query-side tensors (q, do: [H_q, L_c, d]) and the chunk for the
 key/value tensors (k, v: [H_kv, L_c, d]), so every rank sees the same chunks.
 
@@ -14,7 +15,7 @@ from __future__ import annotations
 
 import numpy as np
 
-TENSOR_IDS = {"q": 1, "k": 2, "v": 3, "do": 4}
+TENSOR_IDS = {"q": 1, "k": 2, "v": 3, "do": 4, "x": 5, "h": 6}
 RMS_EPS = 1e-6
 
 
@@ -91,3 +92,17 @@ def to_torch(arr: np.ndarray, device="cpu"):
     else:
         t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
     return t.to(device)
+
+
+def fir_inputs(key: int, n_cp: int, channels: int, shard_len: int, taps: int, dtype: str):
+    """Signal shards x [N_cp, D, Lc] (shard r drawn with index r) and filters h [D, l_h].
+
+    x ~ N(0, 1); the taps ~ N(0, 1/l_h), so that the output stays of order one. Both rounded to
+    bfloat16 for "bf16" (storage form as in ``make``)."""
+    x = np.stack([normal_f32(key, "x", r, (channels, shard_len)) for r in range(n_cp)])
+    h = normal_f32(key, "h", 0, (channels, taps)) * np.float32(1.0 / np.sqrt(taps))
+    if dtype == "bf16":
+        return bf16_rne_bits(x), bf16_rne_bits(h.astype(np.float32))
+    if dtype == "f32":
+        return x, h.astype(np.float32)
+    raise ValueError(f"unknown dtype {dtype!r}")
