@@ -1,4 +1,4 @@
-"""ctypes binding of libcp_attn.so (the C ABI in include/cp_attn.h).
+"""ctypes binding of libcp_attn.so (the C ABI in include/cp_attn.h and include/cp_fir.h).
 
 Argument marshalling only: tensors are checked for device, dtype, shape and contiguity, then
 their device pointers and torch's current HIP stream are handed to the library. Every step of
@@ -34,6 +34,11 @@ class AttnDesc(ctypes.Structure):
                 ("q_pos0", ctypes.c_int64), ("kv_pos0", ctypes.c_int64),
                 ("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
                 ("accumulate", ctypes.c_int32)]
+
+
+class FirDesc(ctypes.Structure):
+    _fields_ = [("channels", ctypes.c_int32), ("shard_len", ctypes.c_int32),
+                ("taps", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
 class RingDesc(ctypes.Structure):
@@ -94,6 +99,14 @@ def load():
     lib.cp_attn_ring_bwd_striped.argtypes = [ctypes.POINTER(RingDesc), _P, _P, _P, _P, _P, _P,
                                              _P, _P, _P, _P, _P]
     lib.cp_attn_ring_bwd_striped.restype = st
+    lib.cp_fir_local.argtypes = [ctypes.POINTER(FirDesc), _P, _P, _P, _P]
+    lib.cp_fir_local.restype = st
+    lib.cp_fir_pack_halo.argtypes = [ctypes.POINTER(FirDesc), _P, _P, _P]
+    lib.cp_fir_pack_halo.restype = st
+    lib.cp_fir_halo.argtypes = [ctypes.POINTER(FirDesc), _P, _P, _P, _P]
+    lib.cp_fir_halo.restype = st
+    lib.cp_fir_ring.argtypes = [ctypes.POINTER(FirDesc), ctypes.c_int32, _P, _P, _P, _P, _P]
+    lib.cp_fir_ring.restype = st
     lib.cp_attn_status_string.argtypes = [ctypes.c_int32]
     lib.cp_attn_status_string.restype = ctypes.c_char_p
     lib.cp_attn_abi_version.argtypes = []
@@ -364,3 +377,57 @@ def ring_bwd_striped(q, k_chunks, v_chunks, d_o, o, lse, delta_work, dq, dk_chun
                                                   _ptr(delta_work), _ptr(dq), _ptr(dk_chunks),
                                                   _ptr(dv_chunks), _stream()),
                   "cp_attn_ring_bwd_striped", allow_skip=False)
+
+
+# ---- causal FIR convolution (include/cp_fir.h)
+
+def _fir_desc(x, h):
+    channels, shard_len = x.shape[-2], x.shape[-1]
+    return FirDesc(channels, shard_len, h.shape[1], _dtype_code(x))
+
+
+def fir_local(x, h, y):
+    """cp_fir_local: y [D, Lc] fp32 = zero-history causal convolution of x [D, Lc] with
+    h [D, l_h] (same dtype as x)."""
+    _need(x, "x")
+    _need(h, "h", dtype=x.dtype)
+    _need(y, "y", shape=x.shape, dtype=torch.float32)
+    if h.dim() != 2 or h.shape[0] != x.shape[0]:
+        raise ValueError("h must be [channels, taps]")
+    d = _fir_desc(x, h)
+    return _check(load().cp_fir_local(ctypes.byref(d), _ptr(x), _ptr(h), _ptr(y), _stream()),
+                  "cp_fir_local", allow_skip=False)
+
+
+def fir_pack_halo(x, taps, halo):
+    """cp_fir_pack_halo: halo [D, taps - 1] = the last taps - 1 samples of x [D, Lc]."""
+    _need(x, "x")
+    _need(halo, "halo", shape=(x.shape[0], taps - 1), dtype=x.dtype)
+    d = FirDesc(x.shape[0], x.shape[1], int(taps), _dtype_code(x))
+    return _check(load().cp_fir_pack_halo(ctypes.byref(d), _ptr(x), _ptr(halo), _stream()),
+                  "cp_fir_pack_halo", allow_skip=False)
+
+
+def fir_halo(halo, h, y):
+    """cp_fir_halo: y[:, :taps - 1] += boundary terms of the previous shard's tail."""
+    _need(h, "h")
+    _need(halo, "halo", shape=(h.shape[0], h.shape[1] - 1), dtype=h.dtype)
+    _need(y, "y", dtype=torch.float32)
+    d = FirDesc(y.shape[0], y.shape[1], h.shape[1], _dtype_code(h))
+    return _check(load().cp_fir_halo(ctypes.byref(d), _ptr(halo), _ptr(h), _ptr(y), _stream()),
+                  "cp_fir_halo", allow_skip=False)
+
+
+def fir_ring(x_shards, h, halo_work, y_shards):
+    """cp_fir_ring over x_shards [N_cp, D, Lc]; y_shards [N_cp, D, Lc] fp32; halo_work
+    [N_cp, D, taps - 1] scratch in x's dtype (None allowed when taps == 1)."""
+    _need(x_shards, "x_shards")
+    n_cp, channels, lc = x_shards.shape
+    _need(h, "h", dtype=x_shards.dtype)
+    _need(y_shards, "y_shards", shape=x_shards.shape, dtype=torch.float32)
+    if halo_work is not None:
+        _need(halo_work, "halo_work", shape=(n_cp, channels, h.shape[1] - 1), dtype=x_shards.dtype)
+    d = _fir_desc(x_shards, h)
+    return _check(load().cp_fir_ring(ctypes.byref(d), n_cp, _ptr(x_shards), _ptr(h),
+                                     _ptr(halo_work), _ptr(y_shards), _stream()),
+                  "cp_fir_ring", allow_skip=False)

@@ -96,3 +96,43 @@ def fwd_flops(wl: Workload, rank: int) -> float:
 def bwd_flops(wl: Workload, rank: int) -> float:
     """Algorithmic backward flops: the S recompute, dP, dV, dK and dQ products (2*d each)."""
     return 10.0 * wl.head_dim * wl.heads_q * visible_pairs(wl, rank)
+
+
+# ---- causal FIR convolution workloads (StripedHyena 2 context-parallelism page, section 3:
+# the p2p convolution of the short explicit and medium regularized filters). The page names the
+# filter classes but not their lengths; "short" is taken as 7 taps and "medium" as 128.
+
+@dataclass(frozen=True)
+class FirWorkload:
+    key: int
+    name: str
+    dtype: str          # of x, h and the halo
+    channels: int       # D
+    seq_len: int
+    n_cp: int
+    taps: int           # l_h
+    rank: int           # the rank whose share is benchmarked
+    note: str = field(default="", compare=False)
+
+    @property
+    def shard_len(self) -> int:
+        return self.seq_len // self.n_cp
+
+    def flops(self) -> float:
+        """Algorithmic flops of one rank's share: 2 * taps per output (the causal ramp at the
+        start of the sequence is ignored)."""
+        return 2.0 * self.taps * self.channels * self.shard_len
+
+    def bytes(self) -> float:
+        """Algorithmic HBM bytes of one rank's share: x read once, y written once (fp32), the
+        halo read (plus the tail packed for the next rank)."""
+        e = 2 if self.dtype == "bf16" else 4
+        return self.channels * (self.shard_len * (e + 4) + 2 * (self.taps - 1) * e)
+
+
+F1 = FirWorkload(11, "fir-tiny-f32", "f32", 4, 256, 4, 5, 3, note="fp32, 4 shards of 64")
+F2 = FirWorkload(12, "fir-short-208k", "bf16", 4096, 212992, 16, 7, 15,
+                 note="D = 4096, 16 shards of 13,312, 7 taps")
+F3 = FirWorkload(13, "fir-medium-208k", "bf16", 4096, 212992, 16, 128, 15,
+                 note="D = 4096, 16 shards of 13,312, 128 taps")
+FIR_WORKLOADS = {w.key: w for w in (F1, F2, F3)}

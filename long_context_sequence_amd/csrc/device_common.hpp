@@ -146,10 +146,10 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, unsigned 
                                           const void* lds) {
   const unsigned base = __builtin_amdgcn_readfirstlane(
       (unsigned)(uintptr_t)(__attribute__((address_space(3))) const void*)lds);
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "v"(voff), "s"(rsrc), "s"(base)
-               : "memory", "m0");
+               : "v"(voff), "s"(rsrc), "{m0}"(base)
+               : "memory");
 }
 
 // Direct global -> LDS copy of a ROWS x D bf16 tile into the swizzled layout (no registers, no

@@ -49,4 +49,19 @@ hipError_t launch_bwd_prep(long long rows, int head_dim, int is_bf16, const floa
 // which: 1 = dK/dV kernel, 2 = dQ kernel, 3 = both.
 hipError_t launch_bwd_bf16(const BwdParams& p, int which, hipStream_t s);
 
+// Causal FIR convolution. Rows are (shard, channel) pairs of `len` samples; x, y, halo are
+// indexed by row, h by channel (row % channels).
+struct FirParams {
+  const void* x;     // [rows, len] (dtype)
+  const void* h;     // [channels, taps] (dtype)
+  void* halo;        // [rows, taps - 1] (dtype)
+  float* y;          // [rows, len] fp32
+  int channels, len, taps, taps_pad;  // taps_pad: taps rounded up to a multiple of 8
+  int is_bf16;
+};
+hipError_t launch_fir_local(const FirParams& p, long long rows, hipStream_t s);
+hipError_t launch_fir_pack(const FirParams& p, long long rows, hipStream_t s);
+// y rows y_row0 .. y_row0 + rows - 1 take the boundary terms of halo rows 0 .. rows - 1.
+hipError_t launch_fir_halo(const FirParams& p, long long y_row0, long long rows, hipStream_t s);
+
 }  // namespace cpa

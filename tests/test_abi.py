@@ -11,7 +11,7 @@ from long_context_sequence_amd import binding as cp
 from long_context_sequence_amd import configs
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "cp_attn.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in ("cp_attn.h", "cp_fir.h")]
 
 CP_ERR_NULL, CP_ERR_SHAPE, CP_ERR_DTYPE, CP_ERR_ALIGN, CP_ERR_UNSUPPORTED = -1, -2, -3, -4, -5
 
@@ -20,7 +20,7 @@ needs_lib = pytest.mark.skipif(not os.path.exists(cp.lib_path()),
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(cp_\w+)\s*\(", text)))
 
@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("cp_attn_step", "cp_attn_merge", "cp_attn_bwd", "cp_attn_bwd_prep",
                      "cp_ring_schedule", "cp_attn_ring_fwd", "cp_attn_ring_bwd",
-                     "cp_attn_status_string", "cp_attn_abi_version"):
+                     "cp_attn_status_string", "cp_attn_abi_version", "cp_fir_local",
+                     "cp_fir_pack_halo", "cp_fir_halo", "cp_fir_ring"):
         assert required in names
 
 
@@ -130,3 +131,22 @@ def test_ring_schedule_errors():
     assert lib.cp_ring_schedule(4, 0, 0, None, buf) == CP_ERR_NULL
     assert lib.cp_ring_schedule(4, 3, 1, buf, buf) == 4
     assert lib.cp_ring_schedule(4, 0, 1, buf, buf) == 1
+
+
+@needs_lib
+def test_fir_entry_points_validate_first():
+    lib = cp.load()
+    ok = cp.FirDesc(4, 64, 5, cp.CP_BF16)
+    assert lib.cp_fir_local(None, FAKE, FAKE, FAKE, None) == CP_ERR_NULL
+    for bad, status in ((cp.FirDesc(0, 64, 5, 1), CP_ERR_SHAPE), (cp.FirDesc(4, -1, 5, 1), CP_ERR_SHAPE),
+                        (cp.FirDesc(4, 64, 0, 1), CP_ERR_SHAPE), (cp.FirDesc(4, 64, 1025, 1), CP_ERR_SHAPE),
+                        (cp.FirDesc(4, 3, 5, 1), CP_ERR_SHAPE),     # halo longer than a shard
+                        (cp.FirDesc(4, 64, 5, 9), CP_ERR_DTYPE)):
+        assert lib.cp_fir_local(ctypes.byref(bad), FAKE, FAKE, FAKE, None) == status
+    assert lib.cp_fir_local(ctypes.byref(ok), FAKE, None, FAKE, None) == CP_ERR_NULL
+    assert lib.cp_fir_local(ctypes.byref(ok), FAKE, MISALIGNED, FAKE, None) == CP_ERR_ALIGN
+    assert lib.cp_fir_local(ctypes.byref(cp.FirDesc(4, 0, 1, 1)), None, None, None, None) == 0
+    assert lib.cp_fir_pack_halo(ctypes.byref(cp.FirDesc(4, 64, 1, 1)), None, None, None) == 0
+    assert lib.cp_fir_halo(ctypes.byref(ok), FAKE, FAKE, None, None) == CP_ERR_NULL
+    assert lib.cp_fir_ring(ctypes.byref(ok), 0, FAKE, FAKE, FAKE, FAKE, None) == CP_ERR_SHAPE
+    assert lib.cp_fir_ring(ctypes.byref(ok), 2, FAKE, FAKE, None, FAKE, None) == CP_ERR_NULL

@@ -131,3 +131,82 @@ def test_fir_inputs_are_seeded_and_shaped():
     assert not np.array_equal(x[0], x[1])
     xf, hf = inputs.fir_inputs(7, 3, 4, 16, 5, "f32")
     assert np.array_equal(inputs.bf16_rne_bits(xf), x)
+
+
+# ---- GPU parity through the C ABI
+
+def _check_close(got, ref, what, rel=1e-5):
+    err = np.max(np.abs(got - ref)) if ref.size else 0.0
+    scale = max(1.0, float(np.max(np.abs(ref)))) if ref.size else 1.0
+    assert err <= rel * scale, f"{what}: max err {err:.3g} (scale {scale:.3g})"
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("lc,taps", [(2100, 7), (2100, 128), (1001, 9), (64, 1), (15, 16),
+                                     (4099, 1024)])
+def test_fir_ring_matches_oracle(dtype, lc, taps):
+    import torch
+    from long_context_sequence_amd import binding as cp
+
+    n_cp, d = 4, 6
+    xs, h = inputs.fir_inputs(900 + taps, n_cp, d, lc, taps, dtype)
+    ref = oracle.fir_shards(inputs.widen(xs), inputs.widen(h))
+    x_t, h_t = inputs.to_torch(xs, "cuda"), inputs.to_torch(h, "cuda")
+    y = torch.full((n_cp, d, lc), float("nan"), device="cuda")
+    halo = torch.empty((n_cp, d, taps - 1), dtype=x_t.dtype, device="cuda") if taps > 1 else None
+    cp.fir_ring(x_t, h_t, halo, y)
+    torch.cuda.synchronize()
+    _check_close(y.cpu().numpy(), ref, f"ring {dtype} lc={lc} taps={taps}")
+
+
+@pytest.mark.gpu
+def test_fir_stages_separately():
+    """Stage one alone is the zero-history convolution; the packed halo is the previous shard's
+    tail; stage two completes the shard."""
+    import torch
+    from long_context_sequence_amd import binding as cp
+
+    d, lc, taps = 5, 3000, 33
+    xs, h = inputs.fir_inputs(77, 2, d, lc, taps, "bf16")
+    xw, hw = inputs.widen(xs), inputs.widen(h)
+    x_t, h_t = inputs.to_torch(xs, "cuda"), inputs.to_torch(h, "cuda")
+    y = torch.empty((d, lc), device="cuda")
+    cp.fir_local(x_t[1], h_t, y)
+    torch.cuda.synchronize()
+    _check_close(y.cpu().numpy(), oracle.fir_forward(xw[1], hw), "local stage")
+    halo = torch.empty((d, taps - 1), dtype=torch.bfloat16, device="cuda")
+    cp.fir_pack_halo(x_t[0], taps, halo)
+    torch.cuda.synchronize()
+    assert np.array_equal(halo.cpu().view(torch.int16).numpy().view(np.uint16), xs[0][:, lc - taps + 1:])
+    cp.fir_halo(halo, h_t, y)
+    torch.cuda.synchronize()
+    _check_close(y.cpu().numpy(), oracle.fir_shards(xw, hw)[1], "local + halo")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("key", [12, 13])
+def test_fir_full_size_share_sampled_channels(key):
+    """The 208K-token share of rank 15 (D = 4096, 13,312 samples) in the benchmark's launch
+    configuration (local stage over the whole share, halo from shard 14), checked on sampled
+    channels against the oracle on shards 14 and 15 (enough history for l_h <= 13,313)."""
+    import torch
+    from long_context_sequence_amd import binding as cp
+    from long_context_sequence_amd.configs import FIR_WORKLOADS
+
+    wl = FIR_WORKLOADS[key]
+    lc, d, taps = wl.shard_len, wl.channels, wl.taps
+    xs, h = inputs.fir_inputs(wl.key, wl.n_cp, d, lc, taps, wl.dtype)
+    r = wl.rank
+    x_t, h_t = inputs.to_torch(xs[r], "cuda"), inputs.to_torch(h, "cuda")
+    prev = inputs.to_torch(xs[r - 1], "cuda")
+    y = torch.empty((d, lc), device="cuda")
+    halo = torch.empty((d, taps - 1), dtype=torch.bfloat16, device="cuda")
+    cp.fir_pack_halo(prev, taps, halo)
+    cp.fir_local(x_t, h_t, y)
+    cp.fir_halo(halo, h_t, y)
+    torch.cuda.synchronize()
+    chans = np.array([0, 1, d - 1] + list(np.random.default_rng(key).integers(0, d, 5)))
+    pair = np.concatenate([inputs.widen(xs[r - 1][chans]), inputs.widen(xs[r][chans])], axis=1)
+    ref = oracle.fir_forward(pair, inputs.widen(h[chans]))[:, lc:]
+    _check_close(y[chans].cpu().numpy(), ref, wl.name)
