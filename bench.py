@@ -28,6 +28,7 @@ import numpy as np  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+PEAK_F32_VALU_TFLOPS = 157.3  # MI355X fp32 vector (published; counts packed FMA)
 
 
 def parse():
@@ -43,6 +44,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the oracle CPU baseline (0 disables it)")
     ap.add_argument("--no-merge-bench", action="store_true")
+    ap.add_argument("--no-fir-bench", action="store_true",
+                    help="skip the causal FIR convolution leg (short and medium filters)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy first (reference for HBM byte counters)")
     return ap.parse_args()
@@ -190,6 +193,10 @@ def main():
     if not args.no_merge_bench:
         merge_info = bench_merge(cp, torch, o, lse)
 
+    fir_info = None
+    if not args.no_fir_bench:
+        fir_info = [bench_fir(cp, torch, configs.FIR_WORKLOADS[k]) for k in (12, 13)]
+
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(wl, rank, args.cpu_seconds, do_bwd)
@@ -221,6 +228,7 @@ def main():
         "tokens_per_s": round(lc / (ms_step * 1e-3), 1),
         "roofline": roofline,
         "merge_kernel": merge_info,
+        "fir_conv": fir_info,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -252,6 +260,57 @@ def measured_traffic(workload_name, kernel):
         return None
     return {"read_bytes": int(rec["read_bytes"]), "write_bytes": int(rec["write_bytes"]),
             "total_bytes": int(rec["read_bytes"] + rec["write_bytes"])}
+
+
+def bench_fir(cp, torch, wl, reps=20):
+    """One rank's share of the causal FIR convolution (rank 15 of 16: D channels x 13,312
+    samples): pack the tail for the next rank, the local stage, the halo stage with the previous
+    shard's tail. HIP events on the launch stream around each kernel. Algorithmic bytes: x read
+    and y written once (plus the halo); flops 2 * taps per output."""
+    from long_context_sequence_amd import inputs
+
+    r, d, lc, taps = wl.rank, wl.channels, wl.shard_len, wl.taps
+    x = inputs.to_torch(inputs.fir_shard(wl.key, r, d, lc, wl.dtype), "cuda")
+    prev = inputs.to_torch(inputs.fir_shard(wl.key, r - 1, d, lc, wl.dtype), "cuda")
+    h = inputs.to_torch(inputs.fir_filters(wl.key, d, taps, wl.dtype), "cuda")
+    y = torch.empty((d, lc), device="cuda")
+    halo_in = torch.empty((d, taps - 1), dtype=x.dtype, device="cuda")
+    halo_out = torch.empty_like(halo_in)
+    stream = torch.cuda.current_stream()
+    cp.fir_pack_halo(prev, taps, halo_in)          # what rank r - 1 would have sent
+    for _ in range(3):
+        cp.fir_pack_halo(x, taps, halo_out)
+        cp.fir_local(x, h, y)
+        cp.fir_halo(halo_in, h, y)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    for i in range(reps):
+        ev[i][0].record(stream)
+        cp.fir_pack_halo(x, taps, halo_out)
+        ev[i][1].record(stream)
+        cp.fir_local(x, h, y)
+        ev[i][2].record(stream)
+        cp.fir_halo(halo_in, h, y)
+        ev[i][3].record(stream)
+    torch.cuda.synchronize()
+    pack = sum(e[0].elapsed_time(e[1]) for e in ev) / reps
+    local = sum(e[1].elapsed_time(e[2]) for e in ev) / reps
+    halo = sum(e[2].elapsed_time(e[3]) for e in ev) / reps
+    share = pack + local + halo
+    elem = 2 if wl.dtype == "bf16" else 4
+    local_bytes = d * lc * (elem + 4)
+    local_flops = 2.0 * taps * d * lc
+    gbs = local_bytes / (local * 1e-3) / 1e9
+    tfl = local_flops / (local * 1e-3) / 1e12
+    hbm_frac, valu_frac = gbs / PEAK_HBM_GBS, tfl / PEAK_F32_VALU_TFLOPS
+    bound = "hbm" if hbm_frac >= valu_frac else "alu"
+    return {"workload": wl.name, "channels": d, "shard_len": lc, "taps": taps,
+            "ms_pack": round(pack, 4), "ms_local": round(local, 4), "ms_halo": round(halo, 4),
+            "ms_share": round(share, 4),
+            "local_kernel": {"bound": bound, "achieved_GBs": round(gbs, 1),
+                             "hbm_frac": round(hbm_frac, 4), "achieved_TFLOPs": round(tfl, 2),
+                             "valu_frac": round(valu_frac, 4)},
+            "samples_per_s": round(d * lc / (share * 1e-3), 1)}
 
 
 def bench_merge(cp, torch, o, lse):

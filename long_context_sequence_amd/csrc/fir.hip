@@ -145,19 +145,25 @@ __global__ void __launch_bounds__(256) fir_pack_kernel(FirParams p, long long to
   static_cast<T*>(p.halo)[i] = static_cast<const T*>(p.x)[row * p.len + p.len - hl + j];
 }
 
-// Boundary stage: one wavefront per (target row): y[i] += sum_{k > i} h[k] halo[taps-1+i-k].
-// Target row r_y = y_row0 + b reads halo row b.
+// Boundary stage: one wavefront per target row: y[i] += sum_{k > i} h[k] halo[taps-1+i-k],
+// i < taps - 1, with the row's filter and halo staged in LDS first (coalesced loads).
+// Target row y_row0 + b reads halo row b.
 template <typename T>
 __global__ void __launch_bounds__(64) fir_halo_kernel(FirParams p, long long y_row0) {
+  __shared__ float hs[kMaxTaps];
+  __shared__ float tl[kMaxTaps];
   const long long b = blockIdx.x;
   const int c = (int)((y_row0 + b) % p.channels);
   const int hl = p.taps - 1;
   const T* halo = static_cast<const T*>(p.halo) + b * hl;
   const T* h = static_cast<const T*>(p.h) + (long long)c * p.taps;
   float* y = p.y + (y_row0 + b) * p.len;
+  for (int k = threadIdx.x; k < p.taps; k += 64) hs[k] = to_f32(h[k]);
+  for (int j = threadIdx.x; j < hl; j += 64) tl[j] = to_f32(halo[j]);
+  __syncthreads();
   for (int i = threadIdx.x; i < hl; i += 64) {
     float acc = 0.f;
-    for (int k = i + 1; k < p.taps; ++k) acc = __builtin_fmaf(to_f32(h[k]), to_f32(halo[hl + i - k]), acc);
+    for (int k = i + 1; k < p.taps; ++k) acc = __builtin_fmaf(hs[k], tl[hl + i - k], acc);
     y[i] += acc;
   }
 }

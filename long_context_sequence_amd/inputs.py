@@ -94,15 +94,27 @@ def to_torch(arr: np.ndarray, device="cpu"):
     return t.to(device)
 
 
-def fir_inputs(key: int, n_cp: int, channels: int, shard_len: int, taps: int, dtype: str):
-    """Signal shards x [N_cp, D, Lc] (shard r drawn with index r) and filters h [D, l_h].
+def fir_shard(key: int, index: int, channels: int, shard_len: int, dtype: str) -> np.ndarray:
+    """Signal shard `index` [D, Lc] of a convolution workload: x ~ N(0, 1)."""
+    x = normal_f32(key, "x", index, (channels, shard_len))
+    return _store(x, dtype)
 
-    x ~ N(0, 1); the taps ~ N(0, 1/l_h), so that the output stays of order one. Both rounded to
-    bfloat16 for "bf16" (storage form as in ``make``)."""
-    x = np.stack([normal_f32(key, "x", r, (channels, shard_len)) for r in range(n_cp)])
+
+def fir_filters(key: int, channels: int, taps: int, dtype: str) -> np.ndarray:
+    """Filter bank h [D, l_h]: taps ~ N(0, 1/l_h), so the output stays of order one."""
     h = normal_f32(key, "h", 0, (channels, taps)) * np.float32(1.0 / np.sqrt(taps))
+    return _store(h.astype(np.float32), dtype)
+
+
+def fir_inputs(key: int, n_cp: int, channels: int, shard_len: int, taps: int, dtype: str):
+    """All signal shards x [N_cp, D, Lc] (shard r drawn with index r) and the filters h."""
+    x = np.stack([fir_shard(key, r, channels, shard_len, dtype) for r in range(n_cp)])
+    return x, fir_filters(key, channels, taps, dtype)
+
+
+def _store(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
-        return bf16_rne_bits(x), bf16_rne_bits(h.astype(np.float32))
+        return bf16_rne_bits(x)
     if dtype == "f32":
-        return x, h.astype(np.float32)
+        return x
     raise ValueError(f"unknown dtype {dtype!r}")

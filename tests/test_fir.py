@@ -196,8 +196,9 @@ def test_fir_full_size_share_sampled_channels(key):
 
     wl = FIR_WORKLOADS[key]
     lc, d, taps = wl.shard_len, wl.channels, wl.taps
-    xs, h = inputs.fir_inputs(wl.key, wl.n_cp, d, lc, taps, wl.dtype)
     r = wl.rank
+    xs = {i: inputs.fir_shard(wl.key, i, d, lc, wl.dtype) for i in (r - 1, r)}
+    h = inputs.fir_filters(wl.key, d, taps, wl.dtype)
     x_t, h_t = inputs.to_torch(xs[r], "cuda"), inputs.to_torch(h, "cuda")
     prev = inputs.to_torch(xs[r - 1], "cuda")
     y = torch.empty((d, lc), device="cuda")
