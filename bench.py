@@ -302,14 +302,19 @@ def bench_fir(cp, torch, wl, reps=20):
     local_flops = 2.0 * taps * d * lc
     gbs = local_bytes / (local * 1e-3) / 1e9
     tfl = local_flops / (local * 1e-3) / 1e12
-    hbm_frac, valu_frac = gbs / PEAK_HBM_GBS, tfl / PEAK_F32_VALU_TFLOPS
-    bound = "hbm" if hbm_frac >= valu_frac else "alu"
+    # the local stage runs on the matrix cores for bf16 filters of 17..256 taps (Toeplitz
+    # product), on the fp32 VALU otherwise; its compute roof is the matching peak
+    on_mfma = wl.dtype == "bf16" and 16 < taps <= 256
+    unit, peak = ("mfma", PEAK_BF16_TFLOPS) if on_mfma else ("alu", PEAK_F32_VALU_TFLOPS)
+    hbm_frac, alu_frac = gbs / PEAK_HBM_GBS, tfl / peak
+    bound = "hbm" if hbm_frac >= alu_frac else unit
     return {"workload": wl.name, "channels": d, "shard_len": lc, "taps": taps,
             "ms_pack": round(pack, 4), "ms_local": round(local, 4), "ms_halo": round(halo, 4),
             "ms_share": round(share, 4),
-            "local_kernel": {"bound": bound, "achieved_GBs": round(gbs, 1),
+            "local_kernel": {"bound": bound, "units": unit, "achieved_GBs": round(gbs, 1),
                              "hbm_frac": round(hbm_frac, 4), "achieved_TFLOPs": round(tfl, 2),
-                             "valu_frac": round(valu_frac, 4)},
+                             "compute_frac": round(alu_frac, 4),
+                             "bytes_per_launch": local_bytes},
             "samples_per_s": round(d * lc / (share * 1e-3), 1)}
 
 

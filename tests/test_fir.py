@@ -144,7 +144,8 @@ def _check_close(got, ref, what, rel=1e-5):
 @pytest.mark.gpu
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("lc,taps", [(2100, 7), (2100, 128), (1001, 9), (64, 1), (15, 16),
-                                     (4099, 1024)])
+                                     (4099, 1024), (1003, 33), (4100, 256), (40, 17), (31, 32),
+                                     (9000, 257)])
 def test_fir_ring_matches_oracle(dtype, lc, taps):
     import torch
     from long_context_sequence_amd import binding as cp
