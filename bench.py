@@ -235,7 +235,9 @@ def main():
 
 
 KERNEL_SOURCES = {"fwd_bf16_kernel": "fwd_bf16.hip", "bwd_kernel": "bwd_bf16.hip",
-                  "merge_kernel": "elementwise.hip", "prep_kernel": "elementwise.hip"}
+                  "merge_kernel": "elementwise.hip", "prep_kernel": "elementwise.hip",
+                  "fir_local_kernel": "fir.hip", "fir_local_mfma_kernel": "fir.hip",
+                  "fir_pack_kernel": "fir.hip", "fir_halo_kernel": "fir.hip"}
 
 
 def measured_traffic(workload_name, kernel):
