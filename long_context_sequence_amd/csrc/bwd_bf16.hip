@@ -347,7 +347,17 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int w, char* sme
   const int dpos = causal_shift(p.q_pos0, p.kv_pos0);
   const int wave_row0 = q_base + 32 * wave;
 
-  for (int kt = 0; kt < n_kt; ++kt) {
+  // Key tiles that every row of the workgroup sees in full (and that lie inside the chunk) come
+  // first: they run without any mask code. The rest (the diagonal and the ragged end) follow.
+  int n_full = p.len_kv / kKT;
+  if (p.causal) {
+    const long long lim = (long long)dpos + q_base + 1;  // keys < lim visible to row q_base
+    n_full = (int)max(0LL, min<long long>(n_full, lim / kKT));
+  }
+  n_full = min(n_full, n_kt);
+
+  auto tile = [&](int kt, auto fullc) {
+    constexpr bool kFull = decltype(fullc)::value;
     const int buf = kt & 1;
     if (kt + 1 < n_kt) {
       Dma::issue(kg, (kt + 1) * kKT, p.len_kv, SK(buf ^ 1), wave, lane);
@@ -386,15 +396,23 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int w, char* sme
           [&](int i) { return tile_col8<D>(SK(buf), 32 * blk + 16 * (i / NB), 32 * (i % NB), lane); },
           [&](int i, const u32x4_t& a) { dqt[i % NB] = mfma32x32x16(a, dsb[i / NB], dqt[i % NB]); });
     };
-    const bool need_mask =
-        key0 + kKT > p.len_kv || (p.causal && key0 + kKT - 1 - wave_row0 > dpos);
-    if (!p.causal || key0 - (wave_row0 + 31) <= dpos) {
-      do_block(0, need_mask);
-      do_block(1, need_mask);
+    if constexpr (kFull) {
+      do_block(0, false);
+      do_block(1, false);
+    } else {
+      const bool need_mask =
+          key0 + kKT > p.len_kv || (p.causal && key0 + kKT - 1 - wave_row0 > dpos);
+      if (!p.causal || key0 - (wave_row0 + 31) <= dpos) {
+        do_block(0, need_mask);
+        do_block(1, need_mask);
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-  }
+  };
+  int kt = 0;
+  for (; kt < n_full; ++kt) tile(kt, std::true_type{});
+  for (; kt < n_kt; ++kt) tile(kt, std::false_type{});
 
   if (!q_ok) return;
   float* dqr = p.dq + ((size_t)h * p.len_q + qi) * D;
