@@ -99,37 +99,6 @@ __device__ __forceinline__ u32x4_t tile_col8(const uint16_t* t, int r0, int c0, 
   return u32x4_t{w0[0], w0[1], w1[0], w1[1]};
 }
 
-// Copies a ROWS x D bf16 tile (rows row0.. of a row-major [nrows, D] array, zero past nrows)
-// from global memory into registers (load) and then into a swizzled LDS tile (store), with
-// NT threads; 16 consecutive lanes cover one 256-byte row, so the global loads are coalesced.
-template <int D, int ROWS, int NT>
-struct TileStager {
-  static constexpr int CH = D / 8;
-  static constexpr int LD = ROWS * CH / NT;
-  static_assert(ROWS * CH % NT == 0, "tile must split evenly over the threads");
-  u32x4_t r[LD];
-  __device__ __forceinline__ void load(const uint16_t* src, int row0, int nrows, int tid) {
-#pragma unroll
-    for (int u = 0; u < LD; ++u) {
-      const int idx = tid + u * NT;
-      const int rr = idx / CH, c = idx % CH;
-      const int row = row0 + rr;
-      const bool ok = row < nrows;
-      const int rc = ok ? row : nrows - 1;
-      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(src + (size_t)rc * D + 8 * c);
-      r[u] = ok ? x : u32x4_t{0u, 0u, 0u, 0u};
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* dst, int tid) const {
-#pragma unroll
-    for (int u = 0; u < LD; ++u) {
-      const int idx = tid + u * NT;
-      const int rr = idx / CH, c = idx % CH;
-      *reinterpret_cast<u32x4_t*>(dst + tile_off<D>(rr, c)) = r[u];
-    }
-  }
-};
-
 // Buffer resource over `bytes` bytes at `base`: loads past the end return zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -158,7 +127,7 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, unsigned 
 // belongs at its slot. The tile's first row goes into the buffer descriptor's base (scalar
 // arithmetic), so the per-lane offsets stay loop-invariant; rows at or past `nrows` read as
 // zeros. Completion is tracked by vmcnt: wait for it before the barrier that publishes the tile.
-// `wave` must be wave-uniform (from readfirstlane) so the LDS base stays scalar.
+// `wave` is the caller's wavefront index (the same in every lane).
 template <int D, int ROWS, int NT>
 struct TileDma {
   static constexpr int CH = D / 8;                 // 16-byte chunks per row
