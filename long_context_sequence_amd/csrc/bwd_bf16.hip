@@ -255,8 +255,23 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* sme
     };
     if (!p.causal || wave_key0 + 31 - q0 <= dpos) {
       // every key of the wave is visible to every row of the tile: no mask, no branches
-      do_block(0, false);
-      do_block(1, false);
+      if constexpr (DV) {
+        // the dV part has one S chain per block: run the two blocks' chains interleaved, so that
+        // consecutive MFMAs never wait for each other's accumulator
+        f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{}, unused = f32x16_t{};
+        u32x4_t pb0[2], pb1[2];
+        mfma_chains<KS, CP_BWD_PF_KV, true>(
+            [&](int ks) { return tile_row8<D>(SQ(buf), perm_row(col), 2 * ks + half); },
+            [&](int ks) { return tile_row8<D>(SQ(buf), 32 + perm_row(col), 2 * ks + half); }, kb,
+            kb, s0, s1);
+        soft(0, s0, unused, false, pb0);
+        soft(1, s1, unused, false, pb1);
+        accum(0, pb0);
+        accum(1, pb1);
+      } else {
+        do_block(0, false);
+        do_block(1, false);
+      }
     } else {
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
