@@ -58,6 +58,20 @@ def test_small_ragged_gqa_all_ranks(d, causal):
             assert np.all(dk[r + 1:] == 0) and np.all(dv[r + 1:] == 0)
 
 
+@pytest.mark.parametrize("hq,hkv", [(8, 1), (3, 3)])
+def test_head_groupings(hq, hkv):
+    """Multi-query (8 query heads share one key/value head: dK/dV sum over all 8) and odd-count
+    multi-head attention, 136-row chunks."""
+    wl = small_workload(203, "bf16", hq, hkv, 128, 136, 3, True, backward=True)
+    for r in range(wl.n_cp):
+        dq, dk, dv = _ring_fwd_bwd(wl, r)
+        q, k, v, do = host_inputs(wl, r, with_do=True)
+        dq_ref, dk_ref, dv_ref = oracle.rank_backward(q, k, v, do, r, True)
+        _check_grad(dq, dq_ref, f"dQ rank {r}")
+        _check_grad(dk, dk_ref, f"dK rank {r}")
+        _check_grad(dv, dv_ref, f"dV rank {r}")
+
+
 @pytest.mark.parametrize("q0,k0,causal", [
     (0, 0, True),        # diagonal
     (400, 0, True),      # fully visible

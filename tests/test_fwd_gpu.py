@@ -46,6 +46,17 @@ def test_small_ragged_gqa_all_ranks(d, causal, fused):
         check_o_lse(o, lse, o_ref, lse_ref, "bf16", f"rank {r}")
 
 
+@pytest.mark.parametrize("hq,hkv", [(8, 1), (16, 2), (3, 3)])
+def test_head_groupings(hq, hkv):
+    """Multi-query (8 query heads on 1 key/value head), group 8, and plain multi-head attention
+    with an odd head count, on 136-row chunks (ragged against every tile size)."""
+    wl = small_workload(103, "bf16", hq, hkv, 128, 136, 3, True)
+    for r in range(wl.n_cp):
+        o, lse = _ring_gpu(wl, r, True)
+        o_ref, lse_ref = oracle_rank(wl, r)
+        check_o_lse(o, lse, o_ref, lse_ref, "bf16", f"H {hq}/{hkv} rank {r}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("q0,k0,causal,accumulate", [
     (0, 0, True, False),      # diagonal
