@@ -161,9 +161,18 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* sme
   // value for it: thread t < kQT fetches the LSE of row t (-inf past the end), thread kQT + t
   // (dK part) delta of row t. One value per thread, returned rather than written through a
   // capture, so that it stays in a register.
+  // Tiles are visited head by head, query tiles in order: (head, tile) of the next tile to load
+  // and of the tile being computed advance by one per iteration (no divisions in the loop).
+  int ld_h = g * p.group, ld_qt = qt_first;
+  int cur_qt = qt_first;
   auto load_it = [&](int it, int buf) -> float {
-    const int h = g * p.group + it / per_head;
-    const int q0 = (qt_first + it % per_head) * kQT;
+    (void)it;
+    const int h = ld_h;
+    const int q0 = ld_qt * kQT;
+    if (++ld_qt == n_qt) {
+      ld_qt = qt_first;
+      ++ld_h;
+    }
     const uint16_t* qh = static_cast<const uint16_t*>(p.q) + (size_t)h * p.len_q * D;
     const uint16_t* doh = static_cast<const uint16_t*>(p.d_o) + (size_t)h * p.len_q * D;
     Dma::issue_lean(qh, q0, p.len_q, SQ(buf), wave, lane);
@@ -198,7 +207,8 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* sme
     const int buf = it & 1;
     float stg = 0.f;
     if (it + 1 < n_it) stg = load_it(it + 1, buf ^ 1);
-    const int q0 = (qt_first + it % per_head) * kQT;
+    const int q0 = cur_qt * kQT;
+    if (++cur_qt == n_qt) cur_qt = qt_first;
     // One 32-row block of the tile against the wave's 32 keys, in three steps:
     // chains: S = Q K^T (and dP = dO V^T) on the matrix cores;
     auto chains = [&](int b, f32x16_t& s, f32x16_t& dp, auto pf) {

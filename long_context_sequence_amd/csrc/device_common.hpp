@@ -105,19 +105,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
                                            0x00020000);
 }
 
+// LDS byte offset of a pointer into LDS: the low 32 bits of its generic address (the LDS
+// aperture sits above 4 GB). Cheaper than the address-space cast, which tests for null.
+__device__ __forceinline__ unsigned lds_offset(const void* p) {
+  return (unsigned)(uintptr_t)p;
+}
+
 // One direct global -> LDS load: 16 bytes per lane from `rsrc` at byte offset `voff` into the
-// LDS block starting at `lds` (lane i's bytes land at lds + 16 i). Issued as an explicit
-// instruction rather than through the compiler's builtin, which makes every later LDS read that
-// the compiler cannot prove disjoint from the destination wait for the load (vmcnt), and would
-// so serialise a double-buffered pipeline on its own prefetch. The caller is responsible for
-// completion: s_waitcnt vmcnt(0) and a workgroup barrier before anything reads the block.
+// LDS block starting at byte offset `lds_off` (wave-uniform; lane i's bytes land at
+// lds_off + 16 i). Issued as an explicit instruction rather than through the compiler's
+// builtin, which makes every later LDS read that the compiler cannot prove disjoint from the
+// destination wait for the load (vmcnt), and would so serialise a double-buffered pipeline on
+// its own prefetch. The caller is responsible for completion: s_waitcnt vmcnt(0) and a
+// workgroup barrier before anything reads the block.
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, unsigned voff,
-                                          const void* lds) {
-  const unsigned base = __builtin_amdgcn_readfirstlane(
-      (unsigned)(uintptr_t)(__attribute__((address_space(3))) const void*)lds);
+                                          unsigned lds_off) {
   asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "v"(voff), "s"(rsrc), "{m0}"(base)
+               : "v"(voff), "s"(rsrc), "{m0}"(lds_off)
                : "memory");
 }
 
@@ -135,17 +140,24 @@ struct TileDma {
   static constexpr int NWAVE = NT / 64;
   static constexpr int ITERS = ROWS / (RPI * NWAVE);
   static_assert(ROWS % (RPI * NWAVE) == 0, "tile must split evenly over the waves");
+  // LDS byte offset of this wave's first block of the tile; the wave's later blocks follow at
+  // a fixed stride.
+  __device__ __forceinline__ static unsigned wave_base(const uint16_t* lds_tile, int wave) {
+    return __builtin_amdgcn_readfirstlane(lds_offset(lds_tile + wave * RPI * D));
+  }
+  static constexpr unsigned kStride = NWAVE * RPI * D * 2;  // bytes between a wave's blocks
+
   __device__ __forceinline__ static void issue(const uint16_t* src, int row0, int nrows,
                                                uint16_t* lds_tile, int wave, int lane) {
     const __amdgpu_buffer_rsrc_t rsrc =
         make_rsrc(src + (size_t)row0 * D, (unsigned)(nrows - row0) * D * 2u);
+    const unsigned base = wave_base(lds_tile, wave);
 #pragma unroll
     for (int u = 0; u < ITERS; ++u) {
-      const int rbase = (u * NWAVE + wave) * RPI;
-      const int r = rbase + lane / CH;
+      const int r = (u * NWAVE + wave) * RPI + lane / CH;
       const int c = (lane % CH) ^ tile_swz<D>(r);
       const unsigned voff = ((unsigned)r * D + 8u * c) * 2u;
-      lds_dma16(rsrc, voff, lds_tile + rbase * D);
+      lds_dma16(rsrc, voff, base + u * kStride);
     }
   }
   // Same copy with the tile's row offset folded into each lane's offset instead of the
@@ -154,13 +166,13 @@ struct TileDma {
   __device__ __forceinline__ static void issue_lean(const uint16_t* src, int row0, int nrows,
                                                     uint16_t* lds_tile, int wave, int lane) {
     const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(src, (unsigned)nrows * D * 2u);
+    const unsigned base = wave_base(lds_tile, wave);
 #pragma unroll
     for (int u = 0; u < ITERS; ++u) {
-      const int rbase = (u * NWAVE + wave) * RPI;
-      const int r = rbase + lane / CH;
+      const int r = (u * NWAVE + wave) * RPI + lane / CH;
       const int c = (lane % CH) ^ tile_swz<D>(r);
       const unsigned voff = ((unsigned)(row0 + r) * D + 8u * c) * 2u;
-      lds_dma16(rsrc, voff, lds_tile + rbase * D);
+      lds_dma16(rsrc, voff, base + u * kStride);
     }
   }
 };
