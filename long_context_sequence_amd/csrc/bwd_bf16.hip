@@ -381,9 +381,11 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int w, char* sme
   }
   n_full = min(n_full, n_kt);
 
-  auto tile = [&](int kt, auto fullc) {
+  // `bufc` = kt % 2 as a compile-time constant where the caller knows it (then every LDS address
+  // of the tile is a per-lane base plus an immediate offset), or -1.
+  auto tile = [&](int kt, auto fullc, auto bufc) {
     constexpr bool kFull = decltype(fullc)::value;
-    const int buf = kt & 1;
+    const int buf = decltype(bufc)::value < 0 ? (kt & 1) : decltype(bufc)::value;
     if (kt + 1 < n_kt) {
       Dma::issue(kg, (kt + 1) * kKT, p.len_kv, SK(buf ^ 1), wave, lane);
       Dma::issue(vg, (kt + 1) * kKT, p.len_kv, SV(buf ^ 1), wave, lane);
@@ -436,8 +438,11 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int w, char* sme
     __syncthreads();
   };
   int kt = 0;
-  for (; kt < n_full; ++kt) tile(kt, std::true_type{});
-  for (; kt < n_kt; ++kt) tile(kt, std::false_type{});
+  for (; kt + 1 < n_full; kt += 2) {  // unrolled by two: the buffer index is a constant
+    tile(kt, std::true_type{}, std::integral_constant<int, 0>{});
+    tile(kt + 1, std::true_type{}, std::integral_constant<int, 1>{});
+  }
+  for (; kt < n_kt; ++kt) tile(kt, std::bool_constant<false>{}, std::integral_constant<int, -1>{});
 
   if (!q_ok) return;
   float* dqr = p.dq + ((size_t)h * p.len_q + qi) * D;

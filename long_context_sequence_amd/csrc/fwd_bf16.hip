@@ -36,11 +36,14 @@ namespace {
 #ifndef CP_FWD_KEYS
 #define CP_FWD_KEYS 64
 #endif
+#ifndef CP_FWD_OCC
+#define CP_FWD_OCC 2
+#endif
 constexpr float kTau = 8.f;   // the reference max moves only when a row max grows by more than
                               // this (log2 units): P stays <= 2^8 and most tiles skip the rescale
 
 template <int D, int NW, int kBN>
-__global__ void __launch_bounds__(NW * 64, 2) fwd_bf16_kernel(StepParams p) {
+__global__ void __launch_bounds__(NW * 64, CP_FWD_OCC) fwd_bf16_kernel(StepParams p) {
   constexpr int NT = NW * 64, BM = 32 * NW, KS = D / 16, NB = D / 32;
   constexpr int SB = kBN / 32;  // 32-key blocks per tile
   // LDS: region r holds K tile slot r followed by V tile slot 1 - r, so that the tiles one
