@@ -393,7 +393,10 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int w, char* sme
     const int key0 = kt * kKT;
     // One 32-key block of the tile against the wave's 32 query rows.
     auto do_block = [&](int blk, bool need_mask) {
-      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+      // dP^T accumulates onto -delta of the lane's row, so that dS^T = P^T * dP^T
+      f32x16_t s = f32x16_t{}, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[r] = -del;
       const int arow = 32 * blk + perm_row(col);
       mfma_chains<KS, CP_BWD_PF_DQ, true>(  // S^T and dP^T chains interleaved
           [&](int ks) { return tile_row8<D>(SK(buf), arow, 2 * ks + half); },
@@ -415,7 +418,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int w, char* sme
           const int r = 2 * r2 + e;
           float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -lse2));
           if (need_mask && (r & 7) + 16 * (r >> 3) > klim) pr = 0.f;
-          dsv[e] = pr * (dp[r] - del);
+          dsv[e] = pr * dp[r];
         }
         dsb[r2 >> 2][r2 & 3] = pack_bf16x2(dsv[0], dsv[1]);
       }
