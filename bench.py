@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-merge-bench", action="store_true")
     ap.add_argument("--no-fir-bench", action="store_true",
                     help="skip the causal FIR convolution leg (short and medium filters)")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the sustained-rate probes (MFMA-only kernel, 1 GiB copy)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy first (reference for HBM byte counters)")
     return ap.parse_args()
@@ -197,6 +199,12 @@ def main():
     if not args.no_fir_bench:
         fir_info = [bench_fir(cp, torch, configs.FIR_WORKLOADS[k]) for k in (12, 13)]
 
+    probe = None
+    if not args.no_probe:
+        probe = device_probe(cp, torch)
+        roofline["sustained_peak"] = probe["mfma_bf16_TFLOPs"]
+        roofline["frac_of_sustained"] = round(achieved / probe["mfma_bf16_TFLOPs"], 4)
+
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(wl, rank, args.cpu_seconds, do_bwd)
@@ -229,6 +237,7 @@ def main():
         "roofline": roofline,
         "merge_kernel": merge_info,
         "fir_conv": fir_info,
+        "device_probe": probe,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -318,6 +327,36 @@ def bench_fir(cp, torch, wl, reps=20):
                              "compute_frac": round(alu_frac, 4),
                              "bytes_per_launch": local_bytes},
             "samples_per_s": round(d * lc / (share * 1e-3), 1)}
+
+
+def device_probe(cp, torch, reps=3):
+    """What this device sustains, beside the published peaks that the roofline fractions use:
+    a kernel of nothing but register-fed 32x32x16 bf16 MFMAs on every CU (cp_probe_mfma_bf16),
+    and a 1 GiB copy with 16-byte accesses (cp_probe_copy; 2 GiB moved per copy)."""
+    stream = torch.cuda.current_stream()
+    n_wg, iters = 256 * 8, 2048
+    sink = torch.empty(n_wg * 256, dtype=torch.float32, device="cuda")
+    cp.probe_mfma_bf16(n_wg, 64, sink)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    flops = sum(cp.probe_mfma_bf16(n_wg, iters, sink) for _ in range(reps))
+    t1.record(stream)
+    t1.synchronize()
+    mfma_tf = flops / (t0.elapsed_time(t1) * 1e-3) / 1e12
+    a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    cp.probe_copy(a, b)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    moved = sum(cp.probe_copy(a, b) for _ in range(reps))
+    t1.record(stream)
+    t1.synchronize()
+    copy_gbs = moved / (t0.elapsed_time(t1) * 1e-3) / 1e9
+    del a, b, sink
+    return {"mfma_bf16_TFLOPs": round(mfma_tf, 1), "mfma_frac_of_published": round(mfma_tf / PEAK_BF16_TFLOPS, 4),
+            "copy_GBs": round(copy_gbs, 1), "copy_frac_of_published": round(copy_gbs / PEAK_HBM_GBS, 4)}
 
 
 def bench_merge(cp, torch, o, lse):

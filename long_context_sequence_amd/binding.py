@@ -107,6 +107,10 @@ def load():
     lib.cp_fir_halo.restype = st
     lib.cp_fir_ring.argtypes = [ctypes.POINTER(FirDesc), ctypes.c_int32, _P, _P, _P, _P, _P]
     lib.cp_fir_ring.restype = st
+    lib.cp_probe_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P]
+    lib.cp_probe_mfma_bf16.restype = st
+    lib.cp_probe_copy.argtypes = [ctypes.c_int64, _P, _P, _P]
+    lib.cp_probe_copy.restype = st
     lib.cp_attn_status_string.argtypes = [ctypes.c_int32]
     lib.cp_attn_status_string.restype = ctypes.c_char_p
     lib.cp_attn_abi_version.argtypes = []
@@ -431,3 +435,27 @@ def fir_ring(x_shards, h, halo_work, y_shards):
     return _check(load().cp_fir_ring(ctypes.byref(d), n_cp, _ptr(x_shards), _ptr(h),
                                      _ptr(halo_work), _ptr(y_shards), _stream()),
                   "cp_fir_ring", allow_skip=False)
+
+
+def probe_mfma_bf16(workgroups, iters, sink):
+    """cp_probe_mfma_bf16: enqueue the matrix-core rate probe on the current stream; sink is a
+    float32 device tensor of at least workgroups * 256 elements. Returns the flops it issues."""
+    _need(sink, "sink", dtype=torch.float32)
+    if sink.numel() < workgroups * 256:
+        raise ValueError("sink must hold workgroups * 256 floats")
+    _check(load().cp_probe_mfma_bf16(int(workgroups), int(iters), _ptr(sink), _stream()),
+           "cp_probe_mfma_bf16", allow_skip=False)
+    return float(workgroups) * 4 * iters * 4 * 32768
+
+
+def probe_copy(src, dst):
+    """cp_probe_copy: dst <- src (float32 device tensors of equal size, a multiple of 4
+    elements) on the current stream. Returns the bytes moved (read + written)."""
+    _need(src, "src", dtype=torch.float32)
+    _need(dst, "dst", shape=src.shape, dtype=torch.float32)
+    if src.numel() % 4:
+        raise ValueError("the probe copies whole 16-byte elements")
+    n4 = src.numel() // 4
+    _check(load().cp_probe_copy(n4, _ptr(src), _ptr(dst), _stream()), "cp_probe_copy",
+           allow_skip=False)
+    return 32.0 * n4

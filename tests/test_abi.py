@@ -11,7 +11,7 @@ from long_context_sequence_amd import binding as cp
 from long_context_sequence_amd import configs
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", f) for f in ("cp_attn.h", "cp_fir.h")]
+HEADERS = [os.path.join(ROOT, "include", f) for f in ("cp_attn.h", "cp_fir.h", "cp_probe.h")]
 
 CP_ERR_NULL, CP_ERR_SHAPE, CP_ERR_DTYPE, CP_ERR_ALIGN, CP_ERR_UNSUPPORTED = -1, -2, -3, -4, -5
 
@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
     for required in ("cp_attn_step", "cp_attn_merge", "cp_attn_bwd", "cp_attn_bwd_prep",
                      "cp_ring_schedule", "cp_attn_ring_fwd", "cp_attn_ring_bwd",
                      "cp_attn_status_string", "cp_attn_abi_version", "cp_fir_local",
-                     "cp_fir_pack_halo", "cp_fir_halo", "cp_fir_ring"):
+                     "cp_fir_pack_halo", "cp_fir_halo", "cp_fir_ring", "cp_probe_mfma_bf16", "cp_probe_copy"):
         assert required in names
 
 
@@ -150,3 +150,15 @@ def test_fir_entry_points_validate_first():
     assert lib.cp_fir_halo(ctypes.byref(ok), FAKE, FAKE, None, None) == CP_ERR_NULL
     assert lib.cp_fir_ring(ctypes.byref(ok), 0, FAKE, FAKE, FAKE, FAKE, None) == CP_ERR_SHAPE
     assert lib.cp_fir_ring(ctypes.byref(ok), 2, FAKE, FAKE, None, FAKE, None) == CP_ERR_NULL
+
+
+@needs_lib
+def test_probe_validation():
+    lib = cp.load()
+    assert lib.cp_probe_mfma_bf16(4, 10, None, None) == CP_ERR_NULL
+    assert lib.cp_probe_mfma_bf16(0, 10, FAKE, None) == CP_ERR_SHAPE
+    assert lib.cp_probe_mfma_bf16(4, 0, FAKE, None) == CP_ERR_SHAPE
+    assert lib.cp_probe_mfma_bf16((1 << 20) + 1, 10, FAKE, None) == CP_ERR_SHAPE
+    assert lib.cp_probe_copy(16, None, FAKE, None) == CP_ERR_NULL
+    assert lib.cp_probe_copy(16, ctypes.c_void_p(0x10004), FAKE, None) == CP_ERR_ALIGN
+    assert lib.cp_probe_copy(0, FAKE, FAKE, None) == CP_ERR_SHAPE
