@@ -190,6 +190,48 @@ def attention_backward(q, k, v, d_o, q_pos0=0, kv_pos0=0, causal=False, scale=No
     return dq, dk, dv
 
 
+def attention_backward_rows(q_rows, do_rows, k, v, q_heads, rows, heads_q, q_pos0=0,
+                            kv_pos0=0, causal=False, scale=None, keys=None):
+    """attention_backward restricted to selected query rows, for checks at sizes where the full
+    gradient is out of reach: q_rows[t], do_rows[t] are row rows[t] of query head q_heads[t] (a
+    shard of heads_q heads whose row 0 is at global position q_pos0); k, v [H_kv, L_kv, d] are
+    the full key/value tensors starting at kv_pos0. Each row's softmax, dP and Jacobian term
+    run over all of its visible keys, as in attention_backward.
+
+    Returns dQ of the rows [n, d] and, when `keys` (indices along L_kv) is given, the selected
+    rows' contributions to dK and dV at those keys, [H_kv, len(keys), d] each: the complete
+    dK/dV there when the rows include every row that sees those keys."""
+    q_rows, do_rows = _f64(q_rows), _f64(do_rows)
+    q_heads = np.asarray(q_heads, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    hkv, lk, d = k.shape
+    if heads_q % hkv:
+        raise ValueError("H_q must be a multiple of H_kv")
+    grp = heads_q // hkv
+    sc = _default_scale(scale, d)
+    keys = None if keys is None else np.asarray(keys, dtype=np.int64)
+    dq = np.zeros_like(q_rows)
+    nk = 0 if keys is None else len(keys)
+    dk = np.zeros((hkv, nk, d))
+    dv = np.zeros((hkv, nk, v.shape[2]))
+    for g in np.unique(q_heads // grp):
+        sel = np.nonzero(q_heads // grp == g)[0]
+        kg, vg = _f64(k[g]), _f64(v[g])
+        s = sc * (q_rows[sel] @ kg.T)
+        if causal:
+            vis = (kv_pos0 + np.arange(lk))[None, :] <= (q_pos0 + rows[sel])[:, None]
+            s = np.where(vis, s, -np.inf)
+        _, p = _row_block_softmax(s)
+        dp = do_rows[sel] @ vg.T
+        jac = (p * dp).sum(axis=1, keepdims=True)
+        ds = p * (dp - jac)
+        dq[sel] = sc * (ds @ kg)
+        if nk:
+            dk[g] += sc * (ds[:, keys].T @ q_rows[sel])
+            dv[g] += p[:, keys].T @ do_rows[sel]
+    return dq, dk, dv
+
+
 def softmax_dot(q, k, v, d_o, q_pos0=0, kv_pos0=0, causal=False, scale=None, row_block=512):
     """sum_j P_ij dP_ij per (head, row) [H_q, L_q]: the Jacobian term of attention_backward.
 

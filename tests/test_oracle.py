@@ -252,6 +252,29 @@ def test_attention_rows_agrees_with_attention_forward():
     assert np.max(np.abs(lse2 - lse[heads, rows])) < 1e-13
 
 
+def test_attention_backward_rows_agrees_with_attention_backward():
+    """The row-restricted backward (used at sizes where the full gradient is out of reach)
+    against attention_backward, which autograd and finite differences pin: dQ on any rows;
+    dK/dV at chosen keys from exactly the rows that can see them (causal: query position >=
+    key position), so the partial sums are complete there."""
+    hq, hkv, lq, lk, d = 4, 2, 10, 30, 16
+    q, k, v, do = _rand(hq, lq, d), _rand(hkv, lk, d), _rand(hkv, lk, d), _rand(hq, lq, d)
+    q0 = 20  # query rows at positions 20..29, keys at 0..29
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, q_pos0=q0, causal=True)
+    heads = np.array([0, 3, 1, 2, 3, 0])
+    rows = np.array([0, 9, 4, 1, 2, 5])
+    dq2, _, _ = oracle.attention_backward_rows(q[heads, rows], do[heads, rows], k, v, heads,
+                                               rows, hq, q_pos0=q0, causal=True)
+    assert np.max(np.abs(dq2 - dq[heads, rows])) < 1e-13
+    keys = np.array([25, 29, 27])  # seen by the rows at positions >= 25 only
+    hh, rr = np.meshgrid(np.arange(hq), np.arange(5, lq), indexing="ij")
+    hh, rr = hh.ravel(), rr.ravel()
+    _, dk2, dv2 = oracle.attention_backward_rows(q[hh, rr], do[hh, rr], k, v, hh, rr, hq,
+                                                 q_pos0=q0, causal=True, keys=keys)
+    assert np.max(np.abs(dk2 - dk[:, keys])) < 1e-13
+    assert np.max(np.abs(dv2 - dv[:, keys])) < 1e-13
+
+
 def test_golden_c1_rank0_fixture():
     import json
     import os
