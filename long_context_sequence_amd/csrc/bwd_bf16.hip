@@ -24,8 +24,11 @@ namespace {
 
 constexpr int kQT = 64;    // query rows per tile (dkdv)
 constexpr int kKT = 64;    // keys per tile (dq)
-constexpr int kNW = 4;     // waves per workgroup
-constexpr int kNT = 64 * kNW;
+// Waves per workgroup (NW, a template parameter below): 4 or 8. Each wave owns 32 keys (kv
+// parts) or 32 query rows (dQ part), so NW = 8 halves the tile loads per product (one LDS tile
+// feeds twice the waves) but leaves half as many workgroups to spread over the CUs. The launch
+// takes 8 when the 8-wave grid still has kWideGrid workgroups or more (about eight per CU).
+constexpr int kWideGrid = 2048;
 
 // LDS operand reads issued ahead of their MFMA in the S/dP chains of the kv parts and of the
 // dQ part (0 = compiler's choice). Measured at the 208K shard: the dQ part gains ~7% at 2, the
@@ -106,9 +109,9 @@ constexpr int kv_smem_bytes() { return 2 * 2 * kQT * D * 2 + 2 * 2 * kQT * 4; }
 template <int D>
 constexpr int dq_smem_bytes() { return 2 * 2 * kKT * D * 2; }
 
-template <int D, int PART>
+template <int D, int PART, int NW>
 __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* smem) {
-  constexpr int KS = D / 16, NB = D / 32, BNK = 32 * kNW;
+  constexpr int KS = D / 16, NB = D / 32, BNK = 32 * NW;
   constexpr bool DV = PART == kPartDV;
   uint16_t* const sq_base = reinterpret_cast<uint16_t*>(smem);
   uint16_t* const sdo_base = sq_base + 2 * kQT * D;
@@ -156,7 +159,7 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* sme
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16_t{};
 
-  using Dma = TileDma<D, kQT, kNT>;
+  using Dma = TileDma<D, kQT, 64 * NW>;
   // Issue the direct loads of tile `it` into LDS buffer `buf` and return this thread's staging
   // value for it: thread t < kQT fetches the LSE of row t (-inf past the end), thread kQT + t
   // (dK part) delta of row t. One value per thread, returned rather than written through a
@@ -312,9 +315,9 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* sme
     }
 }
 
-template <int D>
+template <int D, int NW>
 __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int w, char* smem) {
-  constexpr int KS = D / 16, NB = D / 32, BM = 32 * kNW;
+  constexpr int KS = D / 16, NB = D / 32, BM = 32 * NW;
   uint16_t* const sk_base = reinterpret_cast<uint16_t*>(smem);
   uint16_t* const sv_base = sk_base + 2 * kKT * D;
   auto SK = [&](int b) { return sk_base + b * (kKT * D); };
@@ -355,7 +358,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int w, char* sme
 
   const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (size_t)g * p.len_kv * D;
   const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (size_t)g * p.len_kv * D;
-  using Dma = TileDma<D, kKT, kNT>;
+  using Dma = TileDma<D, kKT, 64 * NW>;
 
   f32x16_t dqt[NB];
 #pragma unroll
@@ -464,35 +467,50 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int w, char* sme
 // One launch per ring step: the dK part's workgroups first (the longest), then the dV part's,
 // then the dQ kernel's, so that the short dQ workgroups fill the tail left by the others. The
 // three bodies share one LDS buffer; n_dk, n_dv, n_dq are the segment sizes (0 = segment off).
-template <int D>
-__global__ void __launch_bounds__(kNT, 2) bwd_kernel(BwdParams p, int n_dk, int n_dv, int n_dq) {
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * NW, 2) bwd_kernel(BwdParams p, int n_dk, int n_dv, int n_dq) {
   constexpr int kSmem = kv_smem_bytes<D>() > dq_smem_bytes<D>() ? kv_smem_bytes<D>()
                                                                  : dq_smem_bytes<D>();
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
   int b = blockIdx.x;
   if (b < n_dk) {
-    bwd_kv_body<D, kPartDK>(p, xcd_remap(b, n_dk), smem);
+    bwd_kv_body<D, kPartDK, NW>(p, xcd_remap(b, n_dk), smem);
     return;
   }
   b -= n_dk;
   if (b < n_dv) {
-    bwd_kv_body<D, kPartDV>(p, xcd_remap(b, n_dv), smem);
+    bwd_kv_body<D, kPartDV, NW>(p, xcd_remap(b, n_dv), smem);
     return;
   }
   b -= n_dv;
-  if (b < n_dq) bwd_dq_body<D>(p, xcd_remap(b, n_dq), smem);
+  if (b < n_dq) bwd_dq_body<D, NW>(p, xcd_remap(b, n_dq), smem);
+}
+
+// Workgroups of the launch at NW waves: {dK part, dV part, dQ part}.
+struct BwdGrid {
+  int n_dk, n_dv, n_dq;
+  long long total() const { return (long long)n_dk + n_dv + n_dq; }
+};
+BwdGrid bwd_grid(const BwdParams& p, int which, int nw) {
+  const int rows = 32 * nw;
+  const int n_kv = ((p.len_kv + rows - 1) / rows) * p.heads_kv;
+  const int n_q = ((p.len_q + rows - 1) / rows) * p.heads_q;
+  return {(which & 1) ? n_kv : 0, (which & 1) ? n_kv : 0, (which & 2) ? n_q : 0};
+}
+
+template <int D, int NW>
+hipError_t launch_dn(const BwdParams& p, const BwdGrid& g, hipStream_t s) {
+  hipLaunchKernelGGL((bwd_kernel<D, NW>), dim3((unsigned)g.total()), dim3(64 * NW), 0, s, p,
+                     g.n_dk, g.n_dv, g.n_dq);
+  return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const BwdParams& p, int which, hipStream_t s) {
-  const int n_kv = ((p.len_kv + 32 * kNW - 1) / (32 * kNW)) * p.heads_kv;
-  const int n_q = ((p.len_q + 32 * kNW - 1) / (32 * kNW)) * p.heads_q;
-  const int n_dk = (which & 1) ? n_kv : 0, n_dv = (which & 1) ? n_kv : 0;
-  const int n_dq = (which & 2) ? n_q : 0;
-  const long long total = (long long)n_dk + n_dv + n_dq;
-  if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_kernel<D>), dim3((unsigned)total), dim3(kNT), 0, s, p, n_dk, n_dv, n_dq);
-  return hipGetLastError();
+  const BwdGrid wide = bwd_grid(p, which, 8);
+  if (wide.total() == 0) return hipSuccess;
+  if (wide.total() >= kWideGrid) return launch_dn<D, 8>(p, wide, s);
+  return launch_dn<D, 4>(p, bwd_grid(p, which, 4), s);
 }
 
 }  // namespace

@@ -13,7 +13,7 @@ import oracle
 from long_context_sequence_amd import binding as cp
 from long_context_sequence_amd import configs, inputs
 
-from util import GRAD_REL, device_inputs, host_inputs, small_workload
+from util import GRAD_REL, device_inputs, host_inputs, sample_rows, small_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -177,3 +177,87 @@ def test_c5_full_size_one_head_group():
     e_v = _check_grad(dv[:, g:g + 1], dv_ref, "dV")
     print(f"C5 head group {g}: scaled errors dQ {e_q:.2e} dK {e_k:.2e} dV {e_v:.2e}")
     assert np.max(np.abs(dk.sum(axis=(0, 2)))) <= 2e-2 * np.max(np.abs(dk)) * np.sqrt(8 * 4096)
+
+
+def _wide_grid_workgroups(hq, hkv, lc):
+    # 8-wavefront workgroups of one backward launch: dK and dV parts (256 keys each) and the dQ
+    # part (256 query rows); the launch takes 8-wavefront workgroups from 2048 of them up.
+    tiles = -(-lc // 256)
+    return 2 * tiles * hkv + tiles * hq
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_wide_grid_launch(d):
+    """Backward launches large enough for 8-wavefront workgroups (the configuration of the
+    208K shard), at a size the full oracle checks: 256 query heads over 128 key/value heads,
+    1000-row chunks (ragged against the 256-key and 256-row workgroups and the 64-row tiles),
+    rank 1 of 2 (one diagonal step, one fully visible step)."""
+    hq, hkv, lc = 256, 128, 1000
+    assert _wide_grid_workgroups(hq, hkv, lc) >= 2048
+    wl = small_workload(205, "bf16", hq, hkv, d, lc, 2, True, backward=True)
+    r = 1
+    dq, dk, dv = _ring_fwd_bwd(wl, r)
+    q, k, v, do = host_inputs(wl, r, with_do=True)
+    dq_ref, dk_ref, dv_ref = oracle.rank_backward(q, k, v, do, r, True)
+    _check_grad(dq, dq_ref, "dQ")
+    _check_grad(dk, dk_ref, "dK")
+    _check_grad(dv, dv_ref, "dV")
+
+
+def test_c4_full_size_sampled():
+    """The 208K shard's backward at full size (rank 15 of 16, GQA 32/8, 13,312-row chunks), in
+    the launch configuration the benchmark times. Checked against the oracle on what it can
+    compute row by row: dQ of sampled query rows (each over its 212,992 visible keys), and dK/dV
+    of the last 24 keys of the diagonal chunk for one key/value head, which only the shard's
+    last 24 rows of that head's 4 query heads see. Everything else via identities that hold at
+    any size: sum_j dV_j = sum_i dO_i per head group, sum_j dK_j = 0."""
+    wl = configs.C4
+    r = wl.ranks[-1]
+    lc, grp = wl.chunk_len, wl.group
+    qa = inputs.workload_tensor(wl, "q", r)
+    da = inputs.workload_tensor(wl, "do", r)
+    k_host = inputs.workload_kv(wl, "k")
+    v_host = inputs.workload_kv(wl, "v")
+    q, d_o = inputs.to_torch(qa, "cuda"), inputs.to_torch(da, "cuda")
+    k, v = inputs.to_torch(k_host, "cuda"), inputs.to_torch(v_host, "cuda")
+    o = torch.empty(q.shape, device="cuda")
+    lse = torch.empty(q.shape[:2], device="cuda")
+    cp.ring_fwd(q, k, v, o, lse, r, True)
+    delta = torch.empty_like(lse)
+    dq = torch.zeros_like(o)
+    dk = torch.zeros(k.shape, device="cuda")
+    dv = torch.zeros(v.shape, device="cuda")
+    cp.ring_bwd(q, k, v, d_o, o, lse, delta, dq, dk, dv, r, True)
+    torch.cuda.synchronize()
+    del k, v, o
+    kf = np.concatenate([inputs.bf16_bits_to_f32(c) for c in k_host], axis=1)
+    vf = np.concatenate([inputs.bf16_bits_to_f32(c) for c in v_host], axis=1)
+    qf, dof = inputs.bf16_bits_to_f32(qa), inputs.bf16_bits_to_f32(da)
+
+    heads, rows = sample_rows(wl, r, 12, seed=415)
+    dq_ref, _, _ = oracle.attention_backward_rows(qf[heads, rows], dof[heads, rows], kf, vf,
+                                                  heads, rows, wl.heads_q, q_pos0=r * lc,
+                                                  causal=True, scale=wl.scale)
+    e_q = _check_grad(dq[heads, rows].cpu().numpy(), dq_ref, "dQ (sampled rows)")
+
+    g, n_tail = 5, 24
+    keys = r * lc + np.arange(lc - n_tail, lc)
+    hh, rr = np.meshgrid(np.arange(g * grp, (g + 1) * grp), np.arange(lc - n_tail, lc),
+                         indexing="ij")
+    hh, rr = hh.ravel(), rr.ravel()
+    _, dk_ref, dv_ref = oracle.attention_backward_rows(qf[hh, rr], dof[hh, rr], kf, vf, hh, rr,
+                                                       wl.heads_q, q_pos0=r * lc, causal=True,
+                                                       scale=wl.scale, keys=keys)
+    dk_g = dk[r, g, lc - n_tail:].cpu().numpy()
+    dv_g = dv[r, g, lc - n_tail:].cpu().numpy()
+    e_k = _check_grad(dk_g, dk_ref[g], "dK (diagonal tail keys)")
+    e_v = _check_grad(dv_g, dv_ref[g], "dV (diagonal tail keys)")
+    print(f"C4 backward: scaled errors dQ {e_q:.2e} dK {e_k:.2e} dV {e_v:.2e}")
+
+    # identities over every key of every chunk, per key/value head
+    dk_sum = dk.double().sum(dim=(0, 2)).cpu().numpy()          # [H_kv, d]
+    dv_sum = dv.double().sum(dim=(0, 2)).cpu().numpy()
+    do_sum = torch.from_numpy(dof).double().reshape(wl.heads_kv, grp * lc, -1).sum(dim=1).numpy()
+    assert np.max(np.abs(dv_sum - do_sum)) <= 1e-3 * np.max(np.abs(do_sum))
+    dk_max = float(dk.abs().max())
+    assert np.max(np.abs(dk_sum)) <= 2e-2 * dk_max * np.sqrt(wl.n_cp * lc)
