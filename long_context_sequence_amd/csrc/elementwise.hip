@@ -44,25 +44,36 @@ template <int D, bool BF16>
 __global__ void __launch_bounds__(256) prep_kernel(long long rows, const float* __restrict__ o,
                                                    const void* __restrict__ d_o,
                                                    float* __restrict__ delta) {
-  constexpr int V = D / 4;
+  // 8 elements per thread (two 16-byte loads of O, one of bf16 dO), D/8 threads per row
+  constexpr int V = D / 8;
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long row = idx / V;
   const bool ok = row < rows;
   float acc = 0.f;
   if (ok) {
-    const f32x4_t x = reinterpret_cast<const f32x4_t*>(o)[idx];
-    float g[4];
+    const f32x4_t* op = reinterpret_cast<const f32x4_t*>(o) + 2 * idx;
+    const f32x4_t x0 = __builtin_nontemporal_load(op);
+    const f32x4_t x1 = __builtin_nontemporal_load(op + 1);
+    float g[8];
     if constexpr (BF16) {
-      const u32x2_t w = reinterpret_cast<const u32x2_t*>(d_o)[idx];
-      g[0] = bf16_lo(w[0]);
-      g[1] = bf16_hi(w[0]);
-      g[2] = bf16_lo(w[1]);
-      g[3] = bf16_hi(w[1]);
+      const u32x4_t w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(d_o) + idx);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        g[2 * t] = bf16_lo(w[t]);
+        g[2 * t + 1] = bf16_hi(w[t]);
+      }
     } else {
-      const f32x4_t y = reinterpret_cast<const f32x4_t*>(d_o)[idx];
-      g[0] = y[0]; g[1] = y[1]; g[2] = y[2]; g[3] = y[3];
+      const f32x4_t* yp = reinterpret_cast<const f32x4_t*>(d_o) + 2 * idx;
+      const f32x4_t y0 = __builtin_nontemporal_load(yp);
+      const f32x4_t y1 = __builtin_nontemporal_load(yp + 1);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        g[t] = y0[t];
+        g[4 + t] = y1[t];
+      }
     }
-    acc = x[0] * g[0] + x[1] * g[1] + x[2] * g[2] + x[3] * g[3];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc += x0[t] * g[t] + x1[t] * g[4 + t];
   }
 #pragma unroll
   for (int off = V / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, V);
@@ -81,7 +92,7 @@ hipError_t merge_d(long long rows, float* o_acc, float* lse_acc, const float* o,
 
 template <int D, bool BF16>
 hipError_t prep_d(long long rows, const float* o, const void* d_o, float* delta, hipStream_t s) {
-  const long long threads = rows * (D / 4);
+  const long long threads = rows * (D / 8);
   const long long blocks = (threads + 255) / 256;
   hipLaunchKernelGGL((prep_kernel<D, BF16>), dim3((unsigned)blocks), dim3(256), 0, s, rows, o,
                      d_o, delta);
