@@ -64,7 +64,7 @@ def load():
         return _lib
     if not os.path.exists(_LIB_PATH):
         raise RuntimeError(f"{_LIB_PATH} is missing: build it first "
-                           "(python -c 'import __graft_entry__ as g; g.build()')")
+                           "(python -m long_context_sequence_amd.build)")
     lib = ctypes.CDLL(_LIB_PATH)
     st = ctypes.c_int32
     lib.cp_attn_step.argtypes = [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P]
