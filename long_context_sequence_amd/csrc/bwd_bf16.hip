@@ -25,8 +25,10 @@ namespace {
 constexpr int kQT = 64;    // query rows per tile (dkdv)
 constexpr int kKT = 64;    // keys per tile (dq)
 // Waves per workgroup (NW, a template parameter below): 4 or 8. Each wave owns 32 keys (kv
-// parts) or 32 query rows (dQ part), so NW = 8 halves the tile loads per product (one LDS tile
-// feeds twice the waves) but leaves half as many workgroups to spread over the CUs. The launch
+// parts) or 32 query rows (dQ part). With NW = 8 a kv workgroup covers 128 keys with both parts:
+// waves 0-3 run the dK part and waves 4-7 the dV part on the same keys, so one LDS tile feeds
+// both and each SIMD holds one wave of each kind; a dQ workgroup covers 256 rows. That halves the
+// tile loads per product but leaves half as many workgroups to spread over the CUs: the launch
 // takes 8 when the 8-wave grid still has kWideGrid workgroups or more (about eight per CU).
 constexpr int kWideGrid = 2048;
 
@@ -109,9 +111,11 @@ constexpr int kv_smem_bytes() { return 2 * 2 * kQT * D * 2 + 2 * 2 * kQT * 4; }
 template <int D>
 constexpr int dq_smem_bytes() { return 2 * 2 * kKT * D * 2; }
 
-template <int D, int PART, int NW>
+// KW: waves that split the workgroup's keys (KW = NW, or NW / 2 when the two halves of the
+// workgroup run the dK and the dV part on the same keys and share the tile loads).
+template <int D, int PART, int NW, int KW = NW>
 __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* smem) {
-  constexpr int KS = D / 16, NB = D / 32, BNK = 32 * NW;
+  constexpr int KS = D / 16, NB = D / 32, BNK = 32 * KW;
   constexpr bool DV = PART == kPartDV;
   uint16_t* const sq_base = reinterpret_cast<uint16_t*>(smem);
   uint16_t* const sdo_base = sq_base + 2 * kQT * D;
@@ -129,7 +133,8 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* sme
   const int kv_base = kt * BNK;
 
   // This lane's key: column of the S = Q K^T and dP = dO V^T products.
-  const int key = kv_base + 32 * wave + col;
+  const int kwave = wave % KW;
+  const int key = kv_base + 32 * kwave + col;
   const bool k_ok = key < p.len_kv;
   const int key_c = k_ok ? key : p.len_kv - 1;
   const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (size_t)g * p.len_kv * D;
@@ -204,7 +209,7 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* sme
 
   const float c2 = p.scale_log2;
   const int dpos = causal_shift(p.q_pos0, p.kv_pos0);
-  const int wave_key0 = kv_base + 32 * wave;  // first key of the wave
+  const int wave_key0 = kv_base + 32 * kwave;  // first key of the wave
 
   for (int it = 0; it < n_it; ++it) {
     const int buf = it & 1;
@@ -467,6 +472,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int w, char* sme
 // One launch per ring step: the dK part's workgroups first (the longest), then the dV part's,
 // then the dQ kernel's, so that the short dQ workgroups fill the tail left by the others. The
 // three bodies share one LDS buffer; n_dk, n_dv, n_dq are the segment sizes (0 = segment off).
+// With NW = 8 the first segment holds the mixed dK/dV workgroups and the second is empty.
 template <int D, int NW>
 __global__ void __launch_bounds__(64 * NW, 2) bwd_kernel(BwdParams p, int n_dk, int n_dv, int n_dq) {
   constexpr int kSmem = kv_smem_bytes<D>() > dq_smem_bytes<D>() ? kv_smem_bytes<D>()
@@ -474,7 +480,15 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_kernel(BwdParams p, int n_dk, 
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
   int b = blockIdx.x;
   if (b < n_dk) {
-    bwd_kv_body<D, kPartDK, NW>(p, xcd_remap(b, n_dk), smem);
+    if constexpr (NW == 8) {
+      // waves 0-3: dK part, waves 4-7: dV part, same 128 keys, shared tiles
+      if ((threadIdx.x >> 6) < 4)
+        bwd_kv_body<D, kPartDK, NW, 4>(p, xcd_remap(b, n_dk), smem);
+      else
+        bwd_kv_body<D, kPartDV, NW, 4>(p, xcd_remap(b, n_dk), smem);
+    } else {
+      bwd_kv_body<D, kPartDK, NW>(p, xcd_remap(b, n_dk), smem);
+    }
     return;
   }
   b -= n_dk;
@@ -493,8 +507,12 @@ struct BwdGrid {
 };
 BwdGrid bwd_grid(const BwdParams& p, int which, int nw) {
   const int rows = 32 * nw;
-  const int n_kv = ((p.len_kv + rows - 1) / rows) * p.heads_kv;
   const int n_q = ((p.len_q + rows - 1) / rows) * p.heads_q;
+  if (nw == 8) {  // one workgroup per 128 keys for both parts
+    const int n_mix = ((p.len_kv + 127) / 128) * p.heads_kv;
+    return {(which & 1) ? n_mix : 0, 0, (which & 2) ? n_q : 0};
+  }
+  const int n_kv = ((p.len_kv + rows - 1) / rows) * p.heads_kv;
   return {(which & 1) ? n_kv : 0, (which & 1) ? n_kv : 0, (which & 2) ? n_q : 0};
 }
 
