@@ -3,14 +3,16 @@
 // forward LSE (P = exp(s - LSE)) rather than stored, and delta = rowsum(dO * O) from the prep
 // kernel standing in for sum_j P_ij dP_ij.
 //
-// Three workgroup kinds in one launch, no atomics (every output element has one owner):
-//  * kv (dV part, then dK part): a workgroup owns 128 keys of one key/value head (32 per wave,
-//    held in registers as MFMA operands) and streams the query tiles of every query head of its
-//    group through LDS:
+// Workgroup kinds in one launch, no atomics (every output element has one owner):
+//  * kv (dK part, dV part): a wave owns 32 keys of one key/value head (held in registers as MFMA
+//    operands) and streams the query tiles of every query head of its group through LDS:
 //      S = Q K^T, P = exp2(S*scale*log2e - LSE*log2e)         dV^T += dO^T P      (dV part)
 //      S, P, dP = dO V^T, dS = P (dP - delta)                  dK^T += Q^T dS      (dK part)
-//    (the group's heads summed in registers).
-//  * dq: a workgroup owns 128 query rows of one head (32 per wave) and streams key/value tiles:
+//    (the group's heads summed in registers). With 4-wave workgroups a workgroup runs one part
+//    on 128 keys; with 8-wave workgroups it runs both parts on 128 keys: waves 0-3 the dK
+//    part, waves 4-7 the dV part, on the same keys and the same LDS tiles.
+//  * dq: a wave owns 32 query rows of one head (128 or 256 rows per workgroup) and streams
+//    key/value tiles:
 //      S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T.
 // Transposed operands (dO^T, Q^T, K^T) come from the same row-major LDS tiles through the
 // LDS transpose read. Outputs are accumulated (+=) into fp32 dQ, dK, dV.
