@@ -65,6 +65,23 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     return out
 
 
+ABI_EXAMPLE_SRC = os.path.join(ROOT, "tests", "c_abi_ring.cpp")
+ABI_EXAMPLE = os.path.join(BUILD, "c_abi_ring")
+
+
+def build_abi_example(lib: str = LIB) -> str:
+    """Compile the plain C++ consumer of the C ABI used by the tests (links the in-tree
+    library with an rpath to it); output under _build/."""
+    os.makedirs(BUILD, exist_ok=True)
+    cmd = [hipcc(), "-O2", "-std=c++17", f"--offload-arch={ARCH}", f"-I{INCLUDE}", ABI_EXAMPLE_SRC,
+           "-o", ABI_EXAMPLE, f"-L{os.path.dirname(lib)}", "-lcp_attn",
+           f"-Wl,-rpath,{os.path.dirname(lib)}"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"compiling the ABI example failed:\n{' '.join(cmd)}\n{res.stdout}{res.stderr}")
+    return ABI_EXAMPLE
+
+
 if __name__ == "__main__":
     import argparse
 
@@ -73,3 +90,5 @@ if __name__ == "__main__":
     ap.add_argument("-D", dest="defines", action="append", default=[])
     a = ap.parse_args()
     print(build(verbose=True, out=os.path.abspath(a.out), defines=a.defines))
+    if os.path.abspath(a.out) == LIB:
+        print(build_abi_example())
