@@ -58,6 +58,18 @@ def test_small_ragged_gqa_all_ranks(d, causal):
             assert np.all(dk[r + 1:] == 0) and np.all(dv[r + 1:] == 0)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_single_chunk_ring(causal):
+    """N_cp = 1: the backward ring is one step over the whole sequence."""
+    wl = small_workload(206, "bf16", 4, 2, 128, 300, 1, causal, backward=True)
+    dq, dk, dv = _ring_fwd_bwd(wl, 0)
+    q, k, v, do = host_inputs(wl, 0, with_do=True)
+    dq_ref, dk_ref, dv_ref = oracle.rank_backward(q, k, v, do, 0, causal)
+    _check_grad(dq, dq_ref, "dQ")
+    _check_grad(dk, dk_ref, "dK")
+    _check_grad(dv, dv_ref, "dV")
+
+
 @pytest.mark.parametrize("hq,hkv", [(8, 1), (3, 3)])
 def test_head_groupings(hq, hkv):
     """Multi-query (8 query heads share one key/value head: dK/dV sum over all 8) and odd-count

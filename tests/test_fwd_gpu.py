@@ -46,6 +46,43 @@ def test_small_ragged_gqa_all_ranks(d, causal, fused):
         check_o_lse(o, lse, o_ref, lse_ref, "bf16", f"rank {r}")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_fold_order_does_not_matter(causal):
+    """The ring may deliver chunks in any order: folding the rank's steps into the running
+    (O, LSE) in the ring's order, in reverse and in a shuffled order gives the full-attention
+    result every time, and the orders agree with each other to fp32 rounding."""
+    wl = small_workload(104, "bf16", 8, 2, 128, 160, 4, causal)
+    r = 2
+    q, k, v = device_inputs(wl, r)
+    o_ref, lse_ref = oracle_rank(wl, r)
+    sched = [c for c, cls in cp.ring_schedule(wl.n_cp, r, causal) if cls != 2]
+    orders = [sched, sched[::-1], list(np.random.default_rng(7).permutation(sched))]
+    results = []
+    for order in orders:
+        o = torch.empty(q.shape, device="cuda")
+        lse = torch.empty(q.shape[:2], device="cuda")
+        for i, c in enumerate(order):
+            st = cp.step(q, k[c], v[c], o, lse, q_pos0=r * wl.chunk_len,
+                         kv_pos0=c * wl.chunk_len, causal=causal, accumulate=i > 0)
+            assert st == cp.CP_OK
+        torch.cuda.synchronize()
+        o, lse = o.cpu().numpy(), lse.cpu().numpy()
+        check_o_lse(o, lse, o_ref, lse_ref, "bf16", f"order {list(map(int, order))}")
+        results.append((o, lse))
+    for o, lse in results[1:]:
+        assert np.max(np.abs(o - results[0][0])) <= 1e-5
+        assert np.max(np.abs(lse - results[0][1])) <= 1e-5
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_single_chunk_ring(causal):
+    """N_cp = 1: the ring is one step of plain (causal) attention over the whole sequence."""
+    wl = small_workload(105, "bf16", 4, 2, 128, 300, 1, causal, backward=True)
+    o, lse = _ring_gpu(wl, 0, True)
+    o_ref, lse_ref = oracle_rank(wl, 0)
+    check_o_lse(o, lse, o_ref, lse_ref, "bf16", "N_cp = 1")
+
+
 @pytest.mark.parametrize("hq,hkv", [(8, 1), (16, 2), (3, 3)])
 def test_head_groupings(hq, hkv):
     """Multi-query (8 query heads on 1 key/value head), group 8, and plain multi-head attention
