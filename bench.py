@@ -187,7 +187,10 @@ def main():
     traffic = measured_traffic(wl.name, dom_name.split(" ")[0])
     roofline = {"bound": "mfma", "kernel": dom_name, "achieved": round(achieved, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic["total_bytes"] if traffic else None,
+                "traffic_read_write": ([traffic["read_bytes"], traffic["write_bytes"]]
+                                       if traffic else None),
                 "launches_per_step": n_launch,
                 "avg_launch_ms": round(dom_ms / n_launch, 4)}
 
