@@ -216,6 +216,23 @@ def test_wide_grid_launch(d):
     _check_grad(dv, dv_ref, "dV")
 
 
+@pytest.mark.parametrize("d,causal", [(128, True), (64, False)])
+def test_wide_grid_launch_tiny_rows(d, causal):
+    """The 8-wavefront launch reached through the head count alone: 1024 heads of 5-row
+    chunks (one 128-key workgroup and one 256-row dQ workgroup per head, almost all of it past
+    the end of the chunk)."""
+    hq = hkv = 1024
+    assert _wide_grid_workgroups(hq, hkv, 5) >= 2048
+    wl = small_workload(207, "bf16", hq, hkv, d, 5, 2, causal, backward=True)
+    r = 1
+    dq, dk, dv = _ring_fwd_bwd(wl, r)
+    q, k, v, do = host_inputs(wl, r, with_do=True)
+    dq_ref, dk_ref, dv_ref = oracle.rank_backward(q, k, v, do, r, causal)
+    _check_grad(dq, dq_ref, "dQ")
+    _check_grad(dk, dk_ref, "dK")
+    _check_grad(dv, dv_ref, "dV")
+
+
 def test_c4_full_size_sampled():
     """The 208K shard's backward at full size (rank 15 of 16, GQA 32/8, 13,312-row chunks), in
     the launch configuration the benchmark times. Checked against the oracle on what it can
