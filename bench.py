@@ -196,7 +196,7 @@ def main():
 
     merge_info = None
     if not args.no_merge_bench:
-        merge_info = bench_merge(cp, torch, o, lse)
+        merge_info = bench_merge(cp, torch, o, lse, wl.name)
 
     fir_info = None
     if not args.no_fir_bench:
@@ -362,9 +362,11 @@ def device_probe(cp, torch, reps=3):
             "copy_GBs": round(copy_gbs, 1), "copy_frac_of_published": round(copy_gbs / PEAK_HBM_GBS, 4)}
 
 
-def bench_merge(cp, torch, o, lse):
+def bench_merge(cp, torch, o, lse, workload_name):
     """cp_attn_merge alone on the rank's (O, LSE) shapes: GB/s of algorithmic traffic
-    (read O_acc, O_step, both LSEs; write O_acc, LSE_acc: 12 B per O element + 12 B per row)."""
+    (read O_acc, O_step, both LSEs; write O_acc, LSE_acc: 12 B per O element + 12 B per row),
+    beside the HBM bytes per launch that rocprofv3's FETCH_SIZE/WRITE_SIZE counters measured
+    for this kernel on the same shapes (committed summary; None once the source changed)."""
     o2 = torch.randn_like(o)
     l2 = torch.randn_like(lse)
     oa = torch.randn_like(o)
@@ -382,9 +384,13 @@ def bench_merge(cp, torch, o, lse):
     ms = s.elapsed_time(e) / n
     byts = 12.0 * o.numel() + 12.0 * lse.numel()
     gbs = byts / (ms * 1e-3) / 1e9
-    return {"avg_launch_ms": round(ms, 4), "bytes_per_launch": int(byts),
+    traffic = measured_traffic(workload_name, "merge_kernel")
+    return {"bound": "hbm", "avg_launch_ms": round(ms, 4), "bytes_per_launch": int(byts),
             "achieved_GBs": round(gbs, 1), "peak_GBs": PEAK_HBM_GBS,
-            "frac": round(gbs / PEAK_HBM_GBS, 4)}
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic["total_bytes"] if traffic else None,
+            "traffic_read_write": ([traffic["read_bytes"], traffic["write_bytes"]]
+                                   if traffic else None)}
 
 
 def cpu_baseline(wl, rank, budget_s, with_bwd):

@@ -60,7 +60,10 @@ typedef enum {
 
 typedef enum { CP_F32 = 0, CP_BF16 = 1 } cp_dtype;
 
-/* One ring step: the rank's queries against one key/value chunk. */
+/* One ring step: the rank's queries against one key/value chunk. Positions are explicit
+ * (q_pos0, kv_pos0) rather than chunk indices, so that contiguous, zig-zag and striped
+ * placements all use the same call: for contiguous chunks of length Lc, chunk c starts at
+ * c * Lc. `accumulate` lets a step fold into the running (O, LSE) without a separate merge. */
 typedef struct {
   int32_t heads_q;     /* query heads; a multiple of heads_kv */
   int32_t heads_kv;    /* key/value heads */
@@ -107,15 +110,20 @@ cp_status cp_attn_merge(int64_t rows, int32_t head_dim, float* o_acc, float* lse
 /*
  * cp_attn_bwd_prep — delta[r] = sum_t dO[r, t] * O[r, t] per row (rows = heads_q * len_q), the
  * softmax-Jacobian term the backward needs (since O_i = sum_j P_ij V_j, it equals
- * sum_j P_ij (dO_i . V_j)). O is the final fp32 forward output; d_o has `dtype`.
+ * sum_j P_ij (dO_i . V_j)). O is the final fp32 forward output; d_o has `dtype` (CP_BF16 or
+ * CP_F32), the same [rows, head_dim] layout. delta: [rows] fp32, overwritten.
+ * The pages describe only the forward ring; the backward calls here are the gradient of that
+ * forward (loss = sum(O * dO)) through the softmax Jacobian, with P recomputed from the saved
+ * LSE instead of being stored.
  */
 cp_status cp_attn_bwd_prep(int64_t rows, int32_t head_dim, int32_t dtype, const float* o,
                            const void* d_o, float* delta, void* stream);
 
 /*
  * cp_attn_bwd — one ring step of the backward (dtype CP_BF16): the gradient of
- * loss = sum(O * dO) restricted to this chunk's keys, recomputing P = exp(S - LSE) from the
- * final forward LSE instead of storing it:
+ * loss = sum(O * dO) restricted to this chunk's keys (the gradient of cp_attn_step's forward;
+ * the pages give no backward), recomputing P = exp(S - LSE) from the final forward LSE instead
+ * of storing it:
  *   dV_c += P^T dO,  dP = dO V_c^T,  dS = P * (dP - delta),
  *   dQ += scale * dS K_c,  dK_c += scale * dS^T Q   (dK, dV summed over each head group).
  *   d_o [heads_q, len_q, head_dim] (dtype); lse, delta [heads_q, len_q] fp32 (final forward

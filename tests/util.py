@@ -2,6 +2,9 @@
 the oracle on the same inputs."""
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 import oracle
@@ -69,3 +72,23 @@ def sample_rows(wl, rank, n, seed):
     heads = rng.integers(0, wl.heads_q, n)
     heads[:4] = [0, wl.heads_q - 1, wl.heads_q // 2, 1 % wl.heads_q]
     return heads, rows
+
+
+def host_workers() -> int:
+    """Host cores this process may use (at most 16: one GPU's share of a host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def oracle_map(fn, items):
+    """fn over items on the host cores: a thread pool with BLAS held to one thread per call.
+    numpy releases the GIL inside its array kernels, so the calls run in parallel; threads
+    rather than processes, because this process already holds the GPU."""
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(limits=1, user_api="blas"):
+        with ThreadPoolExecutor(host_workers()) as ex:
+            return list(ex.map(fn, items))
