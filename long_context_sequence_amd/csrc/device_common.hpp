@@ -177,6 +177,22 @@ struct TileDma {
   }
 };
 
+// N matrix products step(i, A_i) whose A operands are LDS reads load(i), each read issued PF
+// products ahead of its use; scheduling fences keep that order (the compiler would otherwise
+// pull reads next to their product and expose the LDS latency).
+template <int N, int PF, typename LA, typename ST>
+__device__ __forceinline__ void mfma_seq(LA load, ST step) {
+  u32x4_t ra[N];
+#pragma unroll
+  for (int i = 0; i < PF && i < N; ++i) ra[i] = load(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i + PF < N) ra[i + PF] = load(i + PF);
+    step(i, ra[i]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Causal visibility in chunk-local coordinates: key j is visible to query i iff
 // kv_pos0 + j <= q_pos0 + i, i.e. j - i <= q_pos0 - kv_pos0. The difference is clamped to a
 // range where the 32-bit test stays exact for local indices below 2^24.

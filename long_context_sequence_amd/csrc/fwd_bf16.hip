@@ -1,26 +1,36 @@
-// One ring step of the forward on gfx950: the rank's query tile against one key/value chunk,
+// One ring step of the forward on gfx950: the rank's query tiles against one key/value chunk,
 // bf16 MFMA for both contractions, online softmax in registers (StripedHyena 2
 // context-parallelism page, section 2, ring attention steps 2-3).
 //
 // Work decomposition
-//   workgroup = NW waves = one query head x BM = 32*NW query rows; each wave owns 32 rows.
-//   Keys stream through LDS in tiles of 64 (double buffered), K and V both row-major.
+//   workgroup = 8 wavefronts in two groups of 4: group A = waves 0-3, group B = waves 4-7.
+//   Waves w and w + 4 share a SIMD. A group owns 128 query rows (32 per wave) of one head.
+//   * pair workgroups: A and B take two heads of the same query tile (in a GQA group both read
+//     the same key/value tiles, loaded once into LDS for both);
+//   * split workgroups: A and B take the same 128 rows of one head and split its keys in two
+//     halves; B hands its partial result to A through LDS at the end. A launch whose pair
+//     workgroups would leave a last, partly filled round on the CUs turns those last pairs into
+//     split workgroups of half the length (and so does a launch too small to fill the chip).
 //
-// Register-level formulation (per wave, per 64-key tile)
+// Ping-pong schedule. Per 64-key tile j a wave runs two phases:
+//   X_j: O^T += V_j^T P_j and S_{j+1}^T = K_{j+1} Q^T          (32 MFMAs, LDS operand reads)
+//   Y_j: P_{j+1} = exp2(S_{j+1}^T * scale*log2e - m), running max/sum, O rescale  (VALU only)
+// Group B runs one phase behind group A, and a workgroup barrier separates consecutive phases,
+// so at any time one wave of each SIMD issues matrix products while the other does the softmax:
+// the VALU work of one hides under the MFMAs of the other.
+//
+// Register-level formulation (per wave, per tile)
 //   S^T[key][query] = K Q^T      A = K rows from LDS, B = the wave's Q rows held in registers
-//   P^T = exp2(S^T * scale*log2e - m)
-//   O^T[d][query] += V^T P^T     A = V^T rows from LDS, B = P^T straight from the S^T
-//                                accumulator registers (no LDS round trip for P)
-// With S^T, each lane's accumulator column is one query row, so the row max needs one swap with
+//   O^T[d][query] += V^T P^T     A = V^T rows from LDS (transpose read), B = P^T straight from
+//                                the S^T accumulator registers (no LDS round trip for P)
+// With S^T, each lane's accumulator column is one query row: the row max needs one swap with
 // the lane 32 apart, the row sum stays lane-local until the end and the O rescale is one scalar
 // per lane. Loading K row perm_row(m) for MFMA row m makes every run of 8 accumulator registers
 // cover 8 consecutive keys, so the matching V^T operand is one transpose read (two
 // ds_read_b64_tr_b16) of the row-major V tile.
 //
-// Causality: the workgroup visits only tiles some of its rows can see; the mask is applied only
-// on tiles that straddle the diagonal (for the wave's rows) or the ragged end of the chunk.
-// Pipelining: S of the next tile is computed on the matrix cores while the VALU turns the
-// current tile's S into P, so each wave keeps both busy.
+// Causality: a group visits only tiles some of its rows can see; the mask is applied only on
+// tiles that straddle the diagonal (for the wave's rows) or the ragged end of the chunk.
 #include <math.h>
 
 #include "device_common.hpp"
@@ -29,119 +39,184 @@
 namespace cpa {
 namespace {
 
-// Launch shape: waves per workgroup (32 query rows each) and keys per LDS tile.
-#ifndef CP_FWD_WAVES
-#define CP_FWD_WAVES 4
+constexpr int kBN = 64;       // keys per LDS tile
+constexpr int kRows = 128;    // query rows per group (32 per wave)
+// LDS operand reads in flight ahead of their product in the matrix phase; raised wave priority
+// during that phase (the softmax wave on the same SIMD yields issue slots to it).
+#ifndef CP_FWD_PF
+#define CP_FWD_PF 4
 #endif
-#ifndef CP_FWD_KEYS
-#define CP_FWD_KEYS 64
+#ifndef CP_FWD_PRIO
+#define CP_FWD_PRIO 1
 #endif
-#ifndef CP_FWD_OCC
-#define CP_FWD_OCC 2
-#endif
+constexpr int kPF = CP_FWD_PF;
 constexpr float kTau = 8.f;   // the reference max moves only when a row max grows by more than
                               // this (log2 units): P stays <= 2^8 and most tiles skip the rescale
 
-template <int D, int NW, int kBN>
-__global__ void __launch_bounds__(NW * 64, CP_FWD_OCC) fwd_bf16_kernel(StepParams p) {
-  constexpr int NT = NW * 64, BM = 32 * NW, KS = D / 16, NB = D / 32;
+// LDS of one group: K slots 0, 1 then V slots 0, 1, one 64 x D bf16 tile each.
+template <int D>
+constexpr int region_elems() { return 4 * kBN * D; }
+
+// What one group of four waves computes: rows [q_base, q_base + 128) of head h against keys
+// [key_lo, key_lo + 64 * n_tiles) of the chunk (its causal extent included).
+struct GroupItem {
+  int h;         // query head (-1: the group idles)
+  int q_base;
+  int key_lo;
+  int n_tiles;
+};
+
+template <int D>
+__global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(StepParams p, int n_pair, int n_split) {
+  constexpr int KS = D / 16, NB = D / 32;
   constexpr int SB = kBN / 32;  // 32-key blocks per tile
-  // LDS: region r holds K tile slot r followed by V tile slot 1 - r, so that the tiles one
-  // iteration fills (K_{j+2}, V_{j+1}) form one region and the tiles it reads (K_{j+1}, V_j)
-  // the other.
   constexpr int kTile = kBN * D;
-  __shared__ __attribute__((aligned(16))) uint16_t sreg[2][2 * kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * region_elems<D>()];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, half = lane >> 5, col = lane & 31;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave_all >> 2;  // 0 = group A, 1 = group B
+  const int wave = wave_all & 3;  // wave within the group
 
-  // Work item: (kv head, query tile from the last one down, head within the group). Items of
-  // one kv head are contiguous and map to one XCD, so its K/V stay in that XCD's L2; the
-  // causally longest tiles start first.
-  const int n_qt = (p.len_q + BM - 1) / BM;
-  const int w = xcd_remap(blockIdx.x, n_qt * p.heads_q);
-  const int h_in = w % p.group;
-  const int rest = w / p.group;
-  const int qt = n_qt - 1 - rest % n_qt;
-  const int g = rest / n_qt;
-  const int h = g * p.group + h_in;
-  const int q_base = qt * BM;
+  const int n_qt = (p.len_q + kRows - 1) / kRows;
+  // Keys any row of tile qt may see.
+  auto key_count = [&](int qt) -> int {
+    const int last_row = min((qt + 1) * kRows, p.len_q) - 1;
+    long long nk = p.len_kv;
+    if (p.causal) nk = min(nk, p.q_pos0 + last_row - p.kv_pos0 + 1);
+    return nk > 0 ? (int)nk : 0;
+  };
+  // Pairs of heads: within a GQA group when its size is even (both heads then read the same
+  // key/value head), else consecutive heads. Work order: pair within its block fastest, then
+  // query tile from the last one down (causally longest first), then block; items of one
+  // key/value head are contiguous and map to one XCD.
+  const bool even_group = (p.group & 1) == 0;
+  const int pairs_per_blk = even_group ? p.group / 2 : (p.heads_q + 1) / 2;
+  const int blk_heads = even_group ? p.group : p.heads_q;
+  auto pair_heads = [&](int w, int& h0, int& h1, int& qt) {
+    const int p_in = w % pairs_per_blk;
+    const int rest = w / pairs_per_blk;
+    qt = n_qt - 1 - rest % n_qt;
+    const int blk = rest / n_qt;
+    h0 = blk * blk_heads + 2 * p_in;
+    h1 = h0 + 1 < p.heads_q ? h0 + 1 : -1;
+  };
 
-  const uint16_t* qh = static_cast<const uint16_t*>(p.q) + (size_t)h * p.len_q * D;
+  GroupItem it;
+  bool split = false;   // both groups on one head, keys split in two halves
+  bool shared = false;  // both groups read the same key/value tiles (loaded by group A)
+  int n_loop;           // tiles both groups step through (the longer group's count)
+  if ((int)blockIdx.x < n_pair) {
+    int h0, h1, qt;
+    pair_heads(xcd_remap(blockIdx.x, n_pair), h0, h1, qt);
+    it.h = grp == 0 ? h0 : h1;
+    it.q_base = qt * kRows;
+    it.key_lo = 0;
+    it.n_tiles = (key_count(qt) + kBN - 1) / kBN;
+    n_loop = it.n_tiles;  // same query tile for both groups: same extent
+    shared = h1 >= 0 && h0 / p.group == h1 / p.group;
+  } else {
+    const int s = xcd_remap(blockIdx.x - n_pair, n_split);
+    int h0, h1, qt;
+    pair_heads(n_pair + s / 2, h0, h1, qt);
+    const int h = (s & 1) ? h1 : h0;
+    if (h < 0) return;  // the whole workgroup idles (odd head count)
+    split = true;
+    const int nt = (key_count(qt) + kBN - 1) / kBN;
+    const int n_a = (nt + 1) / 2;
+    it.h = h;
+    it.q_base = qt * kRows;
+    it.key_lo = grp == 0 ? 0 : n_a * kBN;
+    it.n_tiles = grp == 0 ? n_a : nt - n_a;
+    n_loop = n_a;
+  }
+  const bool active = it.h >= 0;
+  const int g = active ? it.h / p.group : 0;
+  // Tile loads. Separate tiles: each group loads its own K and V. Shared tiles: group A loads
+  // the K tiles, group B the V tiles, so that both groups carry half of the load issue.
+  const bool load_k_own = active && (grp == 0 || !shared);
+  const bool load_v_own = active && (grp == 1 || !shared);
+  const bool v_by_b = shared && grp == 1;  // B's V loads run on the schedule of its Y phases
+  uint16_t* const my_lds = lds + (shared ? 0 : grp) * region_elems<D>();
+  auto KSLOT = [&](int s) { return my_lds + s * kTile; };
+  auto VSLOT = [&](int s) { return my_lds + (2 + s) * kTile; };
+
+  const uint16_t* qh = static_cast<const uint16_t*>(p.q) + (size_t)(active ? it.h : 0) * p.len_q * D;
   const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (size_t)g * p.len_kv * D;
   const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (size_t)g * p.len_kv * D;
 
   // This lane's query row, as the B operand of K Q^T: d = 16*ks + 8*half + t.
-  const int qi = q_base + 32 * wave + col;
-  const bool q_ok = qi < p.len_q;
-  const int qi_c = q_ok ? qi : p.len_q - 1;
+  const int qi = it.q_base + 32 * wave + col;
+  const bool q_ok = active && qi < p.len_q;
+  const int qi_c = q_ok ? qi : 0;
   u32x4_t qreg[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     u32x4_t x = *reinterpret_cast<const u32x4_t*>(qh + (size_t)qi_c * D + 16 * ks + 8 * half);
     qreg[ks] = q_ok ? x : u32x4_t{0u, 0u, 0u, 0u};
   }
-
-  // Keys any row of this workgroup may see.
-  const int last_row = min(q_base + BM, p.len_q) - 1;
-  long long nk = p.len_kv;
-  if (p.causal) nk = min(nk, p.q_pos0 + last_row - p.kv_pos0 + 1);
-  const int n_kt = nk > 0 ? (int)((nk + kBN - 1) / kBN) : 0;
   const int dpos = causal_shift(p.q_pos0, p.kv_pos0);
-  const int wave_row0 = q_base + 32 * wave;
+  const int wave_row0 = it.q_base + 32 * wave;
+  const int n_own = active ? it.n_tiles : 0;
 
-  using Dma = TileDma<D, kBN, NT>;
+  using Dma = TileDma<D, kBN, 256>;
+  // Direct loads of tile t (keys key_lo + 64 t ...) of K or V into a slot.
+  auto load_k = [&](int t, int s) {
+    Dma::issue(kg, it.key_lo + t * kBN, p.len_kv, KSLOT(s), wave, lane);
+  };
+  auto load_v = [&](int t, int s) {
+    Dma::issue(vg, it.key_lo + t * kBN, p.len_kv, VSLOT(s), wave, lane);
+  };
 
   f32x16_t oacc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x16_t{};
   float m_run = -INFINITY;  // reference row max of scale*log2(e)*s
   float l_run = 0.f;        // this lane's share of the running row sum
-
   const float c2 = p.scale_log2;
+  f32x16_t sc[SB];   // S^T of the next tile
+  u32x4_t pb[2 * SB];  // P^T of the current tile, bf16 pairs (the PV operand)
 
-  // S^T = K Q^T of one tile from an LDS buffer; consecutive MFMAs go to different 32-key blocks
-  // (independent accumulators).
-  auto scores = [&](const uint16_t* kt_lds, f32x16_t (&sc)[SB]) {
+  // Phase X_j: O^T += V_j^T P_j (j >= 0), S_{j+1}^T = K_{j+1} Q^T. The products' LDS operands
+  // are read kPF products ahead of their use, with scheduling fences keeping that order: one
+  // wavefront per SIMD issues products in this phase, so nothing else hides the LDS latency.
+  // Product i < 16 is PV (16-key step i / 4, d block i % 4), i >= 16 is S (d step (i-16) / 2,
+  // key block (i-16) % 2).
+  auto pv_load = [&](const uint16_t* v_rd, int i) {
+    return tile_col8<D>(v_rd, 16 * (i / NB), 32 * (i % NB), lane);
+  };
+  auto s_load = [&](const uint16_t* k_rd, int i) {
+    return tile_row8<D>(k_rd, 32 * (i % SB) + perm_row(col), 2 * (i / SB) + half);
+  };
+  auto pv_step = [&](int i, const u32x4_t& a) {
+    oacc[i % NB] = mfma32x32x16(a, pb[i / NB], oacc[i % NB]);
+  };
+  auto s_step = [&](int i, const u32x4_t& a) {
+    sc[i % SB] = mfma32x32x16(a, qreg[i / SB], sc[i % SB]);
+  };
+  constexpr int NPV = 2 * SB * NB, NS = KS * SB;
+  auto zero_s = [&]() {
 #pragma unroll
     for (int blk = 0; blk < SB; ++blk) sc[blk] = f32x16_t{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int blk = 0; blk < SB; ++blk)
-        sc[blk] = mfma32x32x16(tile_row8<D>(kt_lds, 32 * blk + perm_row(col), 2 * ks + half),
-                               qreg[ks], sc[blk]);
   };
-
-  // Software pipeline over key tiles, K one tile ahead of V. During iteration j the wave holds
-  // S_j (computed in iteration j-1) and, while the VALU turns S_j into P_j, the matrix cores
-  // compute S_{j+1}; then O += V_j^T P_j. LDS: K_{j+1} and V_j are resident; the direct loads of
-  // K_{j+2} (into K_j's buffer) and V_{j+1} (into V_{j-1}'s) are in flight.
-  f32x16_t s_a[SB], s_b[SB];  // S of the current tile and of the next one, alternating
-  if (n_kt > 0) {
-    Dma::issue(kg, 0, p.len_kv, sreg[0], wave, lane);           // K_0: K slot 0
-    Dma::issue(vg, 0, p.len_kv, sreg[1] + kTile, wave, lane);   // V_0: V slot 0
-    if (n_kt > 1) Dma::issue(kg, kBN, p.len_kv, sreg[1], wave, lane);  // K_1: K slot 1
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    scores(sreg[0], s_a);
-    __syncthreads();  // every wave is done with K_0 before K_2 lands in its buffer
-  }
-
-  // One iteration. The region it fills by direct loads (wr: K_{j+2} into K slot j%2, V_{j+1}
-  // into V slot (j+1)%2) and the region it reads (rd: K_{j+1}, V_j) are passed as restrict
-  // pointers; knowing they are disjoint, the compiler does not make the LDS reads of V_j wait
-  // for the loads in flight.
-  auto iteration = [&](int kt, uint16_t* __restrict__ wr, const uint16_t* __restrict__ rd,
-                       f32x16_t (&s_cur)[SB], f32x16_t (&s_nxt)[SB]) {
-    uint16_t* const k_wr = wr;
-    uint16_t* const v_wr = wr + kTile;
-    const uint16_t* const k_rd = rd;
-    const uint16_t* const v_rd = rd + kTile;
-    if (kt + 1 < n_kt) Dma::issue(vg, (kt + 1) * kBN, p.len_kv, v_wr, wave, lane);
-    if (kt + 2 < n_kt) Dma::issue(kg, (kt + 2) * kBN, p.len_kv, k_wr, wave, lane);
-    const int key0 = kt * kBN;
+  // X_j inside the loop: both products. On a group's last tile S is computed from the other K
+  // slot (stale but in-bounds) and discarded; the last phase of the loop is peeled instead.
+  auto phase_x = [&](const uint16_t* __restrict__ v_rd, const uint16_t* __restrict__ k_rd) {
+    zero_s();
+    if (CP_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
+    mfma_seq<NPV + NS, kPF>(
+        [&](int i) { return i < NPV ? pv_load(v_rd, i) : s_load(k_rd, i - NPV); },
+        [&](int i, const u32x4_t& a) {
+          if (i < NPV) pv_step(i, a);
+          else s_step(i - NPV, a);
+        });
+    if (CP_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
+  };
+  // Phase Y_j: softmax of S_{j+1}: mask, running max (lazy rescale of O and the sum), P to bf16.
+  auto phase_y = [&](int j) {
+    if (j + 1 >= n_own) return;
+    const int key0 = it.key_lo + (j + 1) * kBN;
     // every key of the tile visible to the wave's first row and inside the chunk?
     const bool full = key0 + kBN <= p.len_kv && (!p.causal || key0 + kBN - 1 - wave_row0 <= dpos);
     if (!full) {
@@ -151,14 +226,14 @@ __global__ void __launch_bounds__(NW * 64, CP_FWD_OCC) fwd_bf16_kernel(StepParam
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + 32 * blk + perm_row(8 * (r >> 2) + 4 * half + (r & 3));
           const bool vis = (key < p.len_kv) & ((!p.causal) | (key - qi <= dpos));
-          s_cur[blk][r] = vis ? s_cur[blk][r] : -INFINITY;
+          sc[blk][r] = vis ? sc[blk][r] : -INFINITY;
         }
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int blk = 0; blk < SB; ++blk)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[blk][r]);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[blk][r]);
     mx = pair_max(mx) * c2;
     // Move the reference max only when the row max outgrew it by more than kTau (the first
     // visible tile always does: m_run starts at -inf). P = exp2(s*c2 - m_run) <= 2^kTau.
@@ -172,17 +247,6 @@ __global__ void __launch_bounds__(NW * 64, CP_FWD_OCC) fwd_bf16_kernel(StepParam
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[nb][r] *= alpha;
     }
-
-    // S_{j+1} on the matrix cores (independent of what follows) ... Unconditional so that it
-    // shares a basic block with the exp work below; on the last tile it reads the other (stale
-    // but in-bounds) K buffer and the result is discarded.
-    scores(k_rd, s_nxt);
-    // Let the scheduler interleave this block's LDS operand reads with the matrix products
-    // (small-GEMM interleave strategy): 3.5% faster than its default schedule here.
-    __builtin_amdgcn_iglp_opt(0);
-
-    // ... while P_j = exp2(S_j*c2 - m) goes to bf16 (PV operand); the row sum stays fp32.
-    u32x4_t pb[2 * SB];
     float lsum = 0.f;
 #pragma unroll
     for (int blk = 0; blk < SB; ++blk)
@@ -190,32 +254,110 @@ __global__ void __launch_bounds__(NW * 64, CP_FWD_OCC) fwd_bf16_kernel(StepParam
       for (int q = 0; q < 2; ++q)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[blk][8 * q + 2 * t], c2, -m_use));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[blk][8 * q + 2 * t + 1], c2, -m_use));
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[blk][8 * q + 2 * t], c2, -m_use));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[blk][8 * q + 2 * t + 1], c2, -m_use));
           pb[2 * blk + q][t] = pack_bf16x2(p0, p1);
           lsum += p0 + p1;
         }
     l_run = l_run * alpha + lsum;
+  };
+  // Workgroup barrier between phases; the scheduling fences keep each phase's instructions on
+  // its own side.
+  auto bar = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-    // O^T += V^T P^T: the V^T operand for keys 16*kk .. 16*kk+15 via the transpose read.
-#pragma unroll
-    for (int kk = 0; kk < 2 * SB; ++kk)
+  // Prologue: K_0, V_0, K_1 of each loading group.
+  if (n_own > 0) {
+    if (load_k_own) {
+      load_k(0, 0);
+      if (n_own > 1) load_k(1, 1);
+    }
+    if (load_v_own) load_v(0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  bar();
+  if (grp == 1) bar();  // group B runs one phase behind
+  if (n_own > 0) {      // X_{-1}: S_0 alone
+    zero_s();
+    mfma_seq<NS, kPF>([&](int i) { return s_load(KSLOT(0), i); }, s_step);
+  }
+  bar();
+  if (v_by_b && 1 < n_own) load_v(1, 1);
+  phase_y(-1);
+  // Tile j: X_j reads V_j (V slot j%2) and K_{j+1} (K slot (j+1)%2). A tile's slot is reused
+  // two tiles later, once both groups have read it (each group reads it in its own X phase,
+  // one phase apart):
+  //  * a group loading its own tiles issues K_{j+2} (into K_j's slot) and V_{j+1} (into
+  //    V_{j-1}'s slot) at the start of X_j and waits for them at the end of Y_j;
+  //  * with shared tiles group B, one phase behind A, issues V_{j+2} (into V_j's slot) at the
+  //    start of its Y_j, after both groups' X_j, and waits for it at the end of its X_{j+1},
+  //    before A's X_{j+2} reads it.
+  // Unrolled by two so that the slots are compile-time constants; the last tile (PV alone)
+  // follows the loop.
+  const int n_body = n_loop - 1;
+  for (int j = 0; j < n_body; j += 2) {
+    bar();
+    if (load_k_own && j + 2 < n_own) load_k(j + 2, 0);
+    if (load_v_own && !v_by_b && j + 1 < n_own) load_v(j + 1, 1);
+    if (j < n_own) phase_x(VSLOT(0), KSLOT(1));
+    if (v_by_b) __builtin_amdgcn_s_waitcnt(0);
+    bar();
+    if (v_by_b && j + 2 < n_own) load_v(j + 2, 0);
+    phase_y(j);
+    if (!v_by_b) __builtin_amdgcn_s_waitcnt(0);
+    if (j + 1 < n_body) {
+      bar();
+      if (load_k_own && j + 3 < n_own) load_k(j + 3, 1);
+      if (load_v_own && !v_by_b && j + 2 < n_own) load_v(j + 2, 0);
+      if (j + 1 < n_own) phase_x(VSLOT(1), KSLOT(0));
+      if (v_by_b) __builtin_amdgcn_s_waitcnt(0);
+      bar();
+      if (v_by_b && j + 3 < n_own) load_v(j + 3, 1);
+      phase_y(j + 1);
+      if (!v_by_b) __builtin_amdgcn_s_waitcnt(0);
+    }
+  }
+  if (n_loop > 0) {  // X of the last tile: PV alone
+    const int j = n_loop - 1;
+    bar();
+    if (j < n_own) {
+      if (CP_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
+      const uint16_t* v_rd = VSLOT(j & 1);
+      mfma_seq<NPV, kPF>([&](int i) { return pv_load(v_rd, i); }, pv_step);
+      if (CP_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
+    }
+    bar();
+  }
+  if (grp == 0) bar();  // group A ends one phase earlier
+
+  if (split) {
+    // B's partial (O^T, running max, its lanes' sums) goes through LDS to A, which folds it into
+    // its own: both are scaled to the larger reference max. The tiles are no longer read.
+    float* const xch = reinterpret_cast<float*>(lds) + wave * (NB * 16 + 2) * 64;
+    if (grp == 1) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        oacc[nb] = mfma32x32x16(tile_col8<D>(v_rd, 16 * kk, 32 * nb, lane), pb[kk], oacc[nb]);
-
-  };
-  // Unrolled by two so that the buffers and the S registers swap roles without copies.
-  for (int kt = 0; kt < n_kt; kt += 2) {
-    iteration(kt, sreg[0], sreg[1], s_a, s_b);
-    // V_{j+1} and K_{j+2} have landed and every wave is done with V_j and K_{j+1}
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (kt + 1 < n_kt) {
-      iteration(kt + 1, sreg[1], sreg[0], s_b, s_a);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xch[(16 * nb + r) * 64 + lane] = oacc[nb][r];
+      xch[(16 * NB) * 64 + lane] = m_run;
+      xch[(16 * NB + 1) * 64 + lane] = l_run;
     }
+    bar();
+    if (grp == 1) return;
+    const float m_b = xch[(16 * NB) * 64 + lane];
+    const float l_b = xch[(16 * NB + 1) * 64 + lane];
+    const float m_new = fmaxf(m_run, m_b);
+    const float wa = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    const float wb = m_b == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_b - m_new);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[nb][r] = wa * oacc[nb][r] + wb * xch[(16 * nb + r) * 64 + lane];
+    l_run = wa * l_run + wb * l_b;
+    m_run = m_new;
   }
 
   // Epilogue: O = O^T / l, LSE = ln(sum exp(s)) = (m + log2 l) * ln 2.
@@ -229,8 +371,8 @@ __global__ void __launch_bounds__(NW * 64, CP_FWD_OCC) fwd_bf16_kernel(StepParam
     inv = 0.f;
     lse_new = -INFINITY;
   }
-  float* orow = p.o + ((size_t)h * p.len_q + qi) * D;
-  float* lrow = p.lse + (size_t)h * p.len_q + qi;
+  float* orow = p.o + ((size_t)it.h * p.len_q + qi) * D;
+  float* lrow = p.lse + (size_t)it.h * p.len_q + qi;
   if (!p.accumulate) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -264,12 +406,35 @@ __global__ void __launch_bounds__(NW * 64, CP_FWD_OCC) fwd_bf16_kernel(StepParam
   }
 }
 
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) cache[dev] = n;
+  return n;
+}
+
 template <int D>
 hipError_t launch_d(const StepParams& p, hipStream_t s) {
-  constexpr int NW = CP_FWD_WAVES, BN = CP_FWD_KEYS;
-  const int n_qt = (p.len_q + 32 * NW - 1) / (32 * NW);
-  const dim3 grid((unsigned)(n_qt * p.heads_q));
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BN>), grid, dim3(NW * 64), 0, s, p);
+  const int n_qt = (p.len_q + kRows - 1) / kRows;
+  const long long n_pairs = (long long)n_qt * ((p.group & 1) == 0 ? p.heads_q / 2
+                                                                   : (p.heads_q + 1) / 2);
+  // One workgroup per CU at a time. If the last round of pair workgroups would fill at most
+  // half of the CUs, its pairs run as split workgroups instead: two per pair, each of half the
+  // length, so the last round takes half the time.
+  const int cus = device_cus();
+  const long long rem = n_pairs % cus;
+  const long long n_split_pairs = (rem > 0 && 2 * rem <= cus) ? rem : 0;
+  const int n_pair = (int)(n_pairs - n_split_pairs);
+  const int n_split = (int)(2 * n_split_pairs);
+  if (n_pair + n_split == 0) return hipSuccess;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D>), dim3((unsigned)(n_pair + n_split)), dim3(512), 0, s,
+                     p, n_pair, n_split);
   return hipGetLastError();
 }
 
