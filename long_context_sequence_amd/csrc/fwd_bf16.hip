@@ -205,11 +205,14 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(StepParams p, int n_pa
   auto phase_x = [&](const uint16_t* __restrict__ v_rd, const uint16_t* __restrict__ k_rd) {
     zero_s();
     if (CP_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
+    // PV and S products alternate: S has two accumulators, and a product must not follow the
+    // product that accumulates into the same registers too closely.
+    static_assert(NPV == NS, "alternating PV and S products");
     mfma_seq<NPV + NS, kPF>(
-        [&](int i) { return i < NPV ? pv_load(v_rd, i) : s_load(k_rd, i - NPV); },
+        [&](int i) { return (i & 1) == 0 ? pv_load(v_rd, i / 2) : s_load(k_rd, i / 2); },
         [&](int i, const u32x4_t& a) {
-          if (i < NPV) pv_step(i, a);
-          else s_step(i - NPV, a);
+          if ((i & 1) == 0) pv_step(i / 2, a);
+          else s_step(i / 2, a);
         });
     if (CP_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
   };
@@ -424,12 +427,17 @@ hipError_t launch_d(const StepParams& p, hipStream_t s) {
   const int n_qt = (p.len_q + kRows - 1) / kRows;
   const long long n_pairs = (long long)n_qt * ((p.group & 1) == 0 ? p.heads_q / 2
                                                                    : (p.heads_q + 1) / 2);
-  // One workgroup per CU at a time. If the last round of pair workgroups would fill at most
-  // half of the CUs, its pairs run as split workgroups instead: two per pair, each of half the
-  // length, so the last round takes half the time.
+  // One workgroup per CU at a time. When every pair has the same work (every key visible to
+  // every row) and the last round of pair workgroups would fill at most half of the CUs, its
+  // pairs run as split workgroups instead: two per pair, each of half the length, so the last
+  // round takes half the time. A launch with fewer pairs than half the CUs is split in full. A
+  // causal step with masking is left whole: its pairs differ in length, the longest run first
+  // and the short ones fill the end.
   const int cus = device_cus();
+  const bool uniform = !p.causal || p.kv_pos0 + p.len_kv - 1 <= p.q_pos0;
   const long long rem = n_pairs % cus;
-  const long long n_split_pairs = (rem > 0 && 2 * rem <= cus) ? rem : 0;
+  const bool split_tail = rem > 0 && 2 * rem <= cus && (uniform || n_pairs < cus);
+  const long long n_split_pairs = split_tail ? rem : 0;
   const int n_pair = (int)(n_pairs - n_split_pairs);
   const int n_split = (int)(2 * n_split_pairs);
   if (n_pair + n_split == 0) return hipSuccess;
