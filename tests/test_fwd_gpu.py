@@ -94,6 +94,21 @@ def test_head_groupings(hq, hkv):
         check_o_lse(o, lse, o_ref, lse_ref, "bf16", f"H {hq}/{hkv} rank {r}")
 
 
+@pytest.mark.parametrize("hq,hkv,causal", [(130, 130, True), (131, 131, False), (195, 65, True),
+                                            (260, 130, True)])
+def test_pair_workgroups_mixed_head_layouts(hq, hkv, causal):
+    """Launches with between half and all of the chip's CUs in head pairs (so every pair runs
+    whole, none split): multi-head pairs on two key/value heads (separate tiles per group), an
+    odd head count (the last pair's second group idles), group 3 (pairs straddle key/value
+    groups) and group 2 (both heads of a pair on one key/value head); 200-row chunks, ring of
+    2, every rank."""
+    wl = small_workload(107, "bf16", hq, hkv, 128, 200, 2, causal)
+    for r in range(wl.n_cp):
+        o, lse = _ring_gpu(wl, r, True)
+        o_ref, lse_ref = oracle_rank(wl, r)
+        check_o_lse(o, lse, o_ref, lse_ref, "bf16", f"H {hq}/{hkv} rank {r}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("q0,k0,causal,accumulate", [
     (0, 0, True, False),      # diagonal
