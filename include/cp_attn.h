@@ -55,7 +55,8 @@ typedef enum {
   CP_ERR_DTYPE = -3,        /* unknown dtype */
   CP_ERR_ALIGN = -4,        /* a pointer is not 16-byte aligned */
   CP_ERR_UNSUPPORTED = -5,  /* valid request this build does not implement (e.g. head_dim 96) */
-  CP_ERR_HIP = -6           /* the HIP runtime reported an error at launch */
+  CP_ERR_HIP = -6,          /* the HIP runtime reported an error at launch */
+  CP_ERR_SCRATCH_LIMIT = -7 /* larger than the fixed scratch of an allocation-free entry point */
 } cp_status;
 
 typedef enum { CP_F32 = 0, CP_BF16 = 1 } cp_dtype;
@@ -192,6 +193,25 @@ cp_status cp_attn_ring_bwd(const cp_ring_desc* ring, const void* q, const void* 
                            const void* v_chunks, const void* d_o, const float* o,
                            const float* lse, float* delta_work, float* dq, float* dk_chunks,
                            float* dv_chunks, void* stream);
+
+/*
+ * cp_attn_ring_bwd_noalloc — cp_attn_ring_bwd for callers that cannot allocate device memory
+ * (code under graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * backward ring, with the per-row delta kept in a fixed device array of the library instead of
+ * a caller-provided delta_work. Same arguments and results as cp_attn_ring_bwd otherwise.
+ *  - Limit: heads_q * chunk_len <= CP_NOALLOC_MAX_ROWS rows (16 MiB of fp32 per device, held
+ *    until the process ends); larger requests return CP_ERR_SCRATCH_LIMIT before anything is
+ *    enqueued.
+ *  - The array is per device and shared by every call on that device, so calls that overlap
+ *    in time on one device (different streams or threads) race; serialize them. The array
+ *    needs no clearing: each call overwrites the rows it reads.
+ *  - Allocates nothing (no hipMalloc); the first call on a device looks the array up once.
+ */
+#define CP_NOALLOC_MAX_ROWS (1 << 22)
+cp_status cp_attn_ring_bwd_noalloc(const cp_ring_desc* ring, const void* q, const void* k_chunks,
+                                   const void* v_chunks, const void* d_o, const float* o,
+                                   const float* lse, float* dq, float* dk_chunks,
+                                   float* dv_chunks, void* stream);
 
 /*
  * Zig-zag causal load balancing (context-parallelism page, section 5: Llama 3's split, which

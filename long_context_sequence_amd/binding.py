@@ -87,6 +87,9 @@ def load():
     lib.cp_attn_ring_bwd.argtypes = [ctypes.POINTER(RingDesc), _P, _P, _P, _P, _P, _P, _P, _P,
                                      _P, _P, _P]
     lib.cp_attn_ring_bwd.restype = st
+    lib.cp_attn_ring_bwd_noalloc.argtypes = [ctypes.POINTER(RingDesc), _P, _P, _P, _P, _P, _P,
+                                             _P, _P, _P, _P]
+    lib.cp_attn_ring_bwd_noalloc.restype = st
     lib.cp_zigzag_shards.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
     lib.cp_zigzag_shards.restype = ctypes.c_int32
     lib.cp_attn_ring_fwd_zigzag.argtypes = [ctypes.POINTER(RingDesc), _P, _P, _P, _P, _P, _P]
@@ -296,6 +299,26 @@ def ring_bwd(q, k_chunks, v_chunks, d_o, o, lse, delta_work, dq, dk_chunks, dv_c
                                           _ptr(d_o), _ptr(o), _ptr(lse), _ptr(delta_work), _ptr(dq),
                                           _ptr(dk_chunks), _ptr(dv_chunks), _stream()),
                   "cp_attn_ring_bwd", allow_skip=False)
+
+
+def ring_bwd_noalloc(q, k_chunks, v_chunks, d_o, o, lse, dq, dk_chunks, dv_chunks, rank,
+                     causal, scale=None):
+    """cp_attn_ring_bwd_noalloc: cp_attn_ring_bwd with the library's fixed delta scratch."""
+    _need(q, "q")
+    _need(k_chunks, "k_chunks", dtype=q.dtype)
+    _need(v_chunks, "v_chunks", shape=k_chunks.shape, dtype=q.dtype)
+    _need(d_o, "d_o", shape=q.shape, dtype=q.dtype)
+    _need(o, "o", shape=q.shape, dtype=torch.float32)
+    _need(lse, "lse", shape=q.shape[:2], dtype=torch.float32)
+    _need(dq, "dq", shape=q.shape, dtype=torch.float32)
+    _need(dk_chunks, "dk_chunks", shape=k_chunks.shape, dtype=torch.float32)
+    _need(dv_chunks, "dv_chunks", shape=k_chunks.shape, dtype=torch.float32)
+    r = _ring(q, k_chunks, rank, causal, scale)
+    return _check(load().cp_attn_ring_bwd_noalloc(ctypes.byref(r), _ptr(q), _ptr(k_chunks),
+                                                  _ptr(v_chunks), _ptr(d_o), _ptr(o), _ptr(lse),
+                                                  _ptr(dq), _ptr(dk_chunks), _ptr(dv_chunks),
+                                                  _stream()),
+                  "cp_attn_ring_bwd_noalloc", allow_skip=False)
 
 
 def zigzag_shards(n_cp: int, rank: int):

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libcp_attn.so")
 ARCH = os.environ.get("CP_ATTN_ARCH", "gfx950")
 
 SOURCES = ["host.cpp", "host_fir.cpp", "fwd_bf16.hip", "fwd_f32.hip", "elementwise.hip",
-           "bwd_bf16.hip", "fir.hip", "probe.hip"]
+           "bwd_bf16.hip", "fir.hip", "probe.hip", "noalloc.hip"]
 
 # Packed fp32 instructions are kept out of the device code (-packed-fp32-ops).
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

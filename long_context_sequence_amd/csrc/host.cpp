@@ -102,6 +102,8 @@ const char* cp_attn_status_string(int32_t status) {
     case CP_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case CP_ERR_UNSUPPORTED: return "valid request not implemented by this build";
     case CP_ERR_HIP: return "HIP runtime error at launch";
+    case CP_ERR_SCRATCH_LIMIT:
+      return "request larger than the fixed scratch of the allocation-free entry point";
     default: return "unknown status";
   }
 }

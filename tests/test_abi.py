@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 @needs_lib
 def test_status_strings_and_version():
     assert cp.abi_version() == 1
-    for st in range(-6, 2):
+    for st in range(-7, 2):
         s = cp.status_string(st)
         assert s and s != "unknown status"
     assert cp.status_string(99) == "unknown status"
@@ -162,3 +162,16 @@ def test_probe_validation():
     assert lib.cp_probe_copy(16, None, FAKE, None) == CP_ERR_NULL
     assert lib.cp_probe_copy(16, ctypes.c_void_p(0x10004), FAKE, None) == CP_ERR_ALIGN
     assert lib.cp_probe_copy(0, FAKE, FAKE, None) == CP_ERR_SHAPE
+
+
+@needs_lib
+def test_noalloc_ring_rejects_rows_beyond_its_scratch():
+    """heads_q * chunk_len above CP_NOALLOC_MAX_ROWS is refused before any pointer is read."""
+    lib = cp.load()
+    r = cp.RingDesc(heads_q=1024, heads_kv=1024, chunk_len=(1 << 22) // 1024 + 1, head_dim=128,
+                    n_cp=2, rank=1, causal=1, scale=0.0, dtype=cp.CP_BF16)
+    st = lib.cp_attn_ring_bwd_noalloc(ctypes.byref(r), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      FAKE, FAKE, None)
+    assert st == -7 and "scratch" in cp.status_string(st)
+    assert lib.cp_attn_ring_bwd_noalloc(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        FAKE, None) == CP_ERR_NULL
