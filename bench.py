@@ -67,6 +67,8 @@ def main():
     wl = configs.WORKLOADS[args.workload]
     rank = wl.ranks[-1] if args.rank is None else args.rank
     do_bwd = not args.fwd_only
+    n_workers = host_workers()
+    pool = start_oracle_pool(n_workers) if args.cpu_seconds > 0 else None
     dev = "cuda"
     torch.cuda.set_device(0)
     cp.load()
@@ -209,8 +211,10 @@ def main():
         roofline["frac_of_sustained"] = round(achieved / probe["mfma_bf16_TFLOPs"], 4)
 
     cpu = None
-    if args.cpu_seconds > 0:
-        cpu = cpu_baseline(wl, rank, args.cpu_seconds, do_bwd)
+    if pool is not None:
+        cpu = cpu_baseline(pool, n_workers, wl, rank, args.cpu_seconds, do_bwd)
+        pool.close()
+        pool.join()
 
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
     out = {
@@ -393,52 +397,93 @@ def bench_merge(cp, torch, o, lse, workload_name):
                                    if traffic else None)}
 
 
-def cpu_baseline(wl, rank, budget_s, with_bwd):
-    """The fp64 oracle on the host cores, on a bounded sample of the same workload: blocks of
-    256 consecutive query rows of one head each, every row against all its visible keys
-    (forward, and the backward of those rows), until the time budget is used."""
-    import oracle
-    from long_context_sequence_amd import inputs
-
+def host_workers() -> int:
+    """Host cores of this process's share (at most 16: one GPU's share of a host)."""
     try:
-        cores = len(os.sched_getaffinity(0))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        cores = os.cpu_count() or 1
-    lc, d = wl.chunk_len, wl.head_dim
-    rows_per_block = 256
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def start_oracle_pool(n):
+    """n worker processes for the oracle baseline, started before anything touches the GPU (so
+    they inherit no GPU state); each holds BLAS to one thread."""
+    import multiprocessing
+
+    return multiprocessing.get_context("spawn").Pool(n, initializer=_oracle_worker_init)
+
+
+def _oracle_worker_init():
+    from threadpoolctl import threadpool_limits
+
+    global _BLAS_LIMIT
+    _BLAS_LIMIT = threadpool_limits(limits=1, user_api="blas")
+
+
+_ORACLE_KV = {}
+
+
+def _oracle_block(task):
+    """One sampled block: `rows` consecutive query rows of query head h of the rank, forward and
+    (with_bwd) backward of the fp64 oracle against every key of the sequence. Returns (visible
+    pairs, seconds)."""
+    import oracle
+    from long_context_sequence_amd import configs, inputs
+
+    key, rank, h, i0, rows, with_bwd = task
+    wl = configs.WORKLOADS[key]
+    g = h // wl.group
+    if (key, g) not in _ORACLE_KV:
+        _ORACLE_KV.clear()
+        kf = np.concatenate([inputs.widen(inputs.workload_tensor(wl, "k", c)[g:g + 1])
+                             for c in range(wl.n_cp)], axis=1)
+        vf = np.concatenate([inputs.widen(inputs.workload_tensor(wl, "v", c)[g:g + 1])
+                             for c in range(wl.n_cp)], axis=1)
+        _ORACLE_KV[(key, g)] = (kf, vf)
+    kf, vf = _ORACLE_KV[(key, g)]
+    lc = wl.chunk_len
+    qb = inputs.widen(inputs.workload_tensor(wl, "q", rank)[h:h + 1, i0:i0 + rows])
+    db = inputs.widen(inputs.workload_tensor(wl, "do", rank)[h:h + 1, i0:i0 + rows])
+    q0 = rank * lc + i0
+    nkeys = kf.shape[1]
+    pairs = sum(min(nkeys, q0 + i + 1) if wl.causal else nkeys for i in range(qb.shape[1]))
+    t = time.perf_counter()
+    oracle.attention_forward(qb, kf, vf, q_pos0=q0, causal=wl.causal, scale=wl.scale)
+    if with_bwd:
+        oracle.attention_backward(qb, kf, vf, db, q_pos0=q0, causal=wl.causal, scale=wl.scale)
+    return pairs, time.perf_counter() - t
+
+
+def cpu_baseline(pool, n_workers, wl, rank, budget_s, with_bwd):
+    """The fp64 oracle on the host cores, on a bounded, seeded sample of the same workload: one
+    block of consecutive query rows per worker process (one BLAS thread each), every row against
+    all its visible keys, forward and backward. The rate is the sample's algorithmic flops (the
+    GPU metric's count: 4*d forward + 10*d backward per visible pair) over the wall time of the
+    whole pool; the rank's full work at that rate is reported as an extrapolation."""
+    d, lc = wl.head_dim, wl.chunk_len
+    # block height: about budget_s of work per worker at ~12 GFLOP/s per core (fp64 numpy)
+    per_pair = (14.0 if with_bwd else 4.0) * d
+    visible = rank * lc + lc // 2 if wl.causal else wl.seq_len
+    rows = int(max(16, min(lc, budget_s * 12e9 / (per_pair * visible))))
     rng = np.random.default_rng(0)
-    qa = inputs.workload_tensor(wl, "q", rank)
-    da = inputs.workload_tensor(wl, "do", rank)
-    # one key/value head (and its group of query heads) for the whole sample
-    g = int(rng.integers(0, wl.heads_kv))
-    kf = np.concatenate([inputs.widen(inputs.workload_tensor(wl, "k", c)[g:g + 1])
-                         for c in range(wl.n_cp)], axis=1)
-    vf = np.concatenate([inputs.widen(inputs.workload_tensor(wl, "v", c)[g:g + 1])
-                         for c in range(wl.n_cp)], axis=1)
-    t_total = 0.0
-    flops = 0.0
-    blocks = 0
-    t_start = time.time()
-    while blocks == 0 or time.time() - t_start < budget_s:
-        h = g * wl.group + int(rng.integers(0, wl.group))
-        i0 = int(rng.integers(0, max(1, lc - rows_per_block)))
-        qb = inputs.widen(qa[h:h + 1, i0:i0 + rows_per_block])
-        db = inputs.widen(da[h:h + 1, i0:i0 + rows_per_block])
-        q0 = rank * lc + i0
-        nkeys = kf.shape[1]
-        pairs = sum(min(nkeys, q0 + i + 1) if wl.causal else nkeys for i in range(qb.shape[1]))
-        t = time.time()
-        oracle.attention_forward(qb, kf, vf, q_pos0=q0, causal=wl.causal, scale=wl.scale)
-        if with_bwd:
-            oracle.attention_backward(qb, kf, vf, db, q_pos0=q0, causal=wl.causal,
-                                      scale=wl.scale)
-        t_total += time.time() - t
-        flops += (14.0 if with_bwd else 4.0) * d * pairs
-        blocks += 1
-    return {"value": round(flops / t_total / 1e12, 5), "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"{blocks} blocks of {rows_per_block} query rows x all visible keys "
-                      f"({'fwd+bwd' if with_bwd else 'fwd'}, fp64 numpy, {t_total:.1f}s)"}
+    tasks = [(wl.key, rank, int(rng.integers(0, wl.heads_q)), int(rng.integers(0, lc - rows + 1)),
+              rows, with_bwd) for _ in range(n_workers)]
+    pool.map(_oracle_block, [(wl.key, rank, t[2], 0, 1, False) for t in tasks])  # warm inputs
+    t0 = time.perf_counter()
+    res = pool.map(_oracle_block, tasks, chunksize=1)
+    wall = time.perf_counter() - t0
+    flops = per_pair * sum(pr for pr, _ in res)
+    rate = flops / wall
+    rank_pairs = (rank * lc * lc + lc * (lc + 1) // 2) if wl.causal else wl.n_cp * lc * lc
+    full = per_pair * wl.heads_q * rank_pairs / rate
+    return {"value": round(rate / 1e12, 5), "unit": "TFLOP/s", "cores": n_workers,
+            "kind": "oracle", "workers": n_workers, "blas_threads_per_worker": 1,
+            "wall_s": round(wall, 2), "gflops_fp64": round(rate / 1e9, 1),
+            "extrapolated_full_rank_s": round(full, 1),
+            "sample": f"{n_workers} blocks of {rows} query rows (one per worker process) x all "
+                      f"visible keys, {'fwd+bwd' if with_bwd else 'fwd'}, fp64 numpy; the full "
+                      f"rank's time is extrapolated from this rate"}
 
 
 if __name__ == "__main__":
