@@ -126,6 +126,16 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, unsigned 
                : "memory");
 }
 
+// Wait until at most N vector-memory operations of this wave are outstanding (LDS and export
+// counters untouched). Vector loads complete in issue order, so this waits for all but the N
+// most recent ones. s_waitcnt encoding of the gfx9 family: vmcnt in bits 3:0 and 15:14, expcnt
+// in 6:4 (7 = no wait), lgkmcnt in 11:8 (15 = no wait).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Direct global -> LDS copy of a ROWS x D bf16 tile into the swizzled layout (no registers, no
 // LDS store instructions). One buffer_load_dwordx4 ... lds per wave fills 1 KB of LDS at
 // consecutive 16-byte slots, i.e. 1024 / (2D) whole rows; each lane fetches the source chunk that

@@ -133,14 +133,15 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(StepParams p, int n_pa
   }
   const bool active = it.h >= 0;
   const int g = active ? it.h / p.group : 0;
-  // Tile loads. Separate tiles: each group loads its own K and V. Shared tiles: group A loads
-  // the K tiles, group B the V tiles, so that both groups carry half of the load issue.
-  const bool load_k_own = active && (grp == 0 || !shared);
-  const bool load_v_own = active && (grp == 1 || !shared);
-  const bool v_by_b = shared && grp == 1;  // B's V loads run on the schedule of its Y phases
-  uint16_t* const my_lds = lds + (shared ? 0 : grp) * region_elems<D>();
+  // LDS slots. Separate tiles: each group has its own region of two K and two V slots. Shared
+  // tiles: one region of three K and three V slots; group A loads the K tiles, group B the V
+  // tiles, so that both groups carry half of the load issue.
+  uint16_t* const my_lds = lds + grp * region_elems<D>();
   auto KSLOT = [&](int s) { return my_lds + s * kTile; };
   auto VSLOT = [&](int s) { return my_lds + (2 + s) * kTile; };
+  auto KSH = [&](int s) { return lds + s * kTile; };
+  auto VSH = [&](int s) { return lds + (3 + s) * kTile; };
+  static_assert(6 * kTile <= 2 * region_elems<D>(), "three shared K and V slots fit");
 
   const uint16_t* qh = static_cast<const uint16_t*>(p.q) + (size_t)(active ? it.h : 0) * p.len_q * D;
   const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (size_t)g * p.len_kv * D;
@@ -162,11 +163,11 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(StepParams p, int n_pa
 
   using Dma = TileDma<D, kBN, 256>;
   // Direct loads of tile t (keys key_lo + 64 t ...) of K or V into a slot.
-  auto load_k = [&](int t, int s) {
-    Dma::issue(kg, it.key_lo + t * kBN, p.len_kv, KSLOT(s), wave, lane);
+  auto load_k = [&](int t, uint16_t* slot) __attribute__((always_inline)) {
+    Dma::issue(kg, it.key_lo + t * kBN, p.len_kv, slot, wave, lane);
   };
-  auto load_v = [&](int t, int s) {
-    Dma::issue(vg, it.key_lo + t * kBN, p.len_kv, VSLOT(s), wave, lane);
+  auto load_v = [&](int t, uint16_t* slot) __attribute__((always_inline)) {
+    Dma::issue(vg, it.key_lo + t * kBN, p.len_kv, slot, wave, lane);
   };
 
   f32x16_t oacc[NB];
@@ -196,13 +197,13 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(StepParams p, int n_pa
     sc[i % SB] = mfma32x32x16(a, qreg[i / SB], sc[i % SB]);
   };
   constexpr int NPV = 2 * SB * NB, NS = KS * SB;
-  auto zero_s = [&]() {
+  auto zero_s = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int blk = 0; blk < SB; ++blk) sc[blk] = f32x16_t{};
   };
   // X_j inside the loop: both products. On a group's last tile S is computed from the other K
   // slot (stale but in-bounds) and discarded; the last phase of the loop is peeled instead.
-  auto phase_x = [&](const uint16_t* __restrict__ v_rd, const uint16_t* __restrict__ k_rd) {
+  auto phase_x = [&](const uint16_t* __restrict__ v_rd, const uint16_t* __restrict__ k_rd) __attribute__((always_inline)) {
     zero_s();
     if (CP_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
     // PV and S products alternate: S has two accumulators, and a product must not follow the
@@ -217,7 +218,7 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(StepParams p, int n_pa
     if (CP_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
   };
   // Phase Y_j: softmax of S_{j+1}: mask, running max (lazy rescale of O and the sum), P to bf16.
-  auto phase_y = [&](int j) {
+  auto phase_y = [&](int j) __attribute__((always_inline)) {
     if (j + 1 >= n_own) return;
     const int key0 = it.key_lo + (j + 1) * kBN;
     // every key of the tile visible to the wave's first row and inside the chunk?
@@ -266,73 +267,112 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(StepParams p, int n_pa
   };
   // Workgroup barrier between phases; the scheduling fences keep each phase's instructions on
   // its own side.
-  auto bar = [&]() {
+  auto bar = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Prologue: K_0, V_0, K_1 of each loading group.
-  if (n_own > 0) {
-    if (load_k_own) {
-      load_k(0, 0);
-      if (n_own > 1) load_k(1, 1);
-    }
-    if (load_v_own) load_v(0, 0);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  bar();
-  if (grp == 1) bar();  // group B runs one phase behind
-  if (n_own > 0) {      // X_{-1}: S_0 alone
+  // X of a last tile: PV alone.
+  auto phase_x_last = [&](const uint16_t* v_rd) __attribute__((always_inline)) {
+    if (CP_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
+    mfma_seq<NPV, kPF>([&](int i) { return pv_load(v_rd, i); }, pv_step);
+    if (CP_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
+  };
+  auto phase_s0 = [&](const uint16_t* k_rd) __attribute__((always_inline)) {  // X_{-1}: S_0 alone
     zero_s();
-    mfma_seq<NS, kPF>([&](int i) { return s_load(KSLOT(0), i); }, s_step);
-  }
-  bar();
-  if (v_by_b && 1 < n_own) load_v(1, 1);
-  phase_y(-1);
-  // Tile j: X_j reads V_j (V slot j%2) and K_{j+1} (K slot (j+1)%2). A tile's slot is reused
-  // two tiles later, once both groups have read it (each group reads it in its own X phase,
-  // one phase apart):
-  //  * a group loading its own tiles issues K_{j+2} (into K_j's slot) and V_{j+1} (into
-  //    V_{j-1}'s slot) at the start of X_j and waits for them at the end of Y_j;
-  //  * with shared tiles group B, one phase behind A, issues V_{j+2} (into V_j's slot) at the
-  //    start of its Y_j, after both groups' X_j, and waits for it at the end of its X_{j+1},
-  //    before A's X_{j+2} reads it.
-  // Unrolled by two so that the slots are compile-time constants; the last tile (PV alone)
-  // follows the loop.
+    mfma_seq<NS, kPF>([&](int i) { return s_load(k_rd, i); }, s_step);
+  };
+  // Tile j: X_j reads V_j and K_{j+1}; Y_j turns S_{j+1} into P_{j+1}. The loops below are
+  // unrolled by the slot count so that slots are compile-time constants; the last tile (PV
+  // alone) follows each loop.
   const int n_body = n_loop - 1;
-  for (int j = 0; j < n_body; j += 2) {
-    bar();
-    if (load_k_own && j + 2 < n_own) load_k(j + 2, 0);
-    if (load_v_own && !v_by_b && j + 1 < n_own) load_v(j + 1, 1);
-    if (j < n_own) phase_x(VSLOT(0), KSLOT(1));
-    if (v_by_b) __builtin_amdgcn_s_waitcnt(0);
-    bar();
-    if (v_by_b && j + 2 < n_own) load_v(j + 2, 0);
-    phase_y(j);
-    if (!v_by_b) __builtin_amdgcn_s_waitcnt(0);
-    if (j + 1 < n_body) {
-      bar();
-      if (load_k_own && j + 3 < n_own) load_k(j + 3, 1);
-      if (load_v_own && !v_by_b && j + 2 < n_own) load_v(j + 2, 0);
-      if (j + 1 < n_own) phase_x(VSLOT(1), KSLOT(0));
-      if (v_by_b) __builtin_amdgcn_s_waitcnt(0);
-      bar();
-      if (v_by_b && j + 3 < n_own) load_v(j + 3, 1);
-      phase_y(j + 1);
-      if (!v_by_b) __builtin_amdgcn_s_waitcnt(0);
+  if (shared) {
+    // Both groups step through the same n tiles, group B one phase behind group A. Tile t sits
+    // in slot t % 3, and each group issues its loads at the start of its X phase, where the
+    // matrix products leave issue slots free: A issues K_{j+3} in X_j (into K_j's slot: both
+    // groups read K_j in X_{j-1}), B issues V_{j+2} in X_j (into V_{j-1}'s slot: both groups
+    // have read V_{j-1} by then). A waits for K_{j+2} at the end of its Y_j, B for V_{j+1} at the
+    // end of its X_j, each just before the barrier ahead of the first reader's X; the wait lets
+    // the group's newer load stay in flight.
+    const int n = n_loop;
+    if (grp == 0) {
+      if (n > 0) load_k(0, KSH(0));
+      if (n > 1) load_k(1, KSH(1));
+    } else {
+      if (n > 0) load_v(0, VSH(0));
     }
-  }
-  if (n_loop > 0) {  // X of the last tile: PV alone
-    const int j = n_loop - 1;
+    __builtin_amdgcn_s_waitcnt(0);
     bar();
-    if (j < n_own) {
-      if (CP_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
-      const uint16_t* v_rd = VSLOT(j & 1);
-      mfma_seq<NPV, kPF>([&](int i) { return pv_load(v_rd, i); }, pv_step);
-      if (CP_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
+    if (grp == 1) bar();  // group B runs one phase behind
+    if (grp == 0 && 2 < n) load_k(2, KSH(2));
+    if (grp == 1 && 1 < n) load_v(1, VSH(1));
+    if (n > 0) phase_s0(KSH(0));
+    bar();
+    phase_y(-1);
+    auto tile = [&](int j, int s) __attribute__((always_inline)) {  // s = j % 3
+      bar();
+      if (grp == 0 && j + 3 < n) load_k(j + 3, KSH(s));
+      if (grp == 1 && j + 2 < n) load_v(j + 2, VSH(s == 0 ? 2 : s - 1));
+      phase_x(VSH(s), KSH(s == 2 ? 0 : s + 1));
+      if (grp == 1) {  // V_{j+1} complete; V_{j+2} may stay in flight
+        if (j + 2 < n) wait_vmcnt<Dma::ITERS>();
+        else wait_vmcnt<0>();
+      }
+      bar();
+      phase_y(j);
+      if (grp == 0) {  // K_{j+2} complete; K_{j+3} may stay in flight
+        if (j + 3 < n) wait_vmcnt<Dma::ITERS>();
+        else wait_vmcnt<0>();
+      }
+    };
+    for (int j = 0; j < n_body; j += 3) {
+      tile(j, 0);
+      if (j + 1 < n_body) {
+        tile(j + 1, 1);
+        if (j + 2 < n_body) tile(j + 2, 2);
+      }
     }
+    if (n > 0) {
+      bar();
+      phase_x_last(VSH((n - 1) % 3));
+      bar();
+    }
+  } else {
+    // Each group loads its own tiles into its own region, two slots each. K_{j+2} (into K_j's
+    // slot) and V_{j+1} (into V_{j-1}'s slot) are issued at the start of X_j and waited for at
+    // the end of Y_j. In a split workgroup group B may have one tile fewer than group A; it
+    // then idles through A's last phase pair.
+    if (n_own > 0) {
+      load_k(0, KSLOT(0));
+      if (n_own > 1) load_k(1, KSLOT(1));
+      load_v(0, VSLOT(0));
+    }
+    __builtin_amdgcn_s_waitcnt(0);
     bar();
+    if (grp == 1) bar();  // group B runs one phase behind
+    if (n_own > 0) phase_s0(KSLOT(0));
+    bar();
+    phase_y(-1);
+    auto tile = [&](int j, int s) __attribute__((always_inline)) {  // s = j % 2
+      bar();
+      if (j + 2 < n_own) load_k(j + 2, KSLOT(s));
+      if (j + 1 < n_own) load_v(j + 1, VSLOT(1 - s));
+      if (j < n_own) phase_x(VSLOT(s), KSLOT(1 - s));
+      bar();
+      phase_y(j);
+      __builtin_amdgcn_s_waitcnt(0);
+    };
+    for (int j = 0; j < n_body; j += 2) {
+      tile(j, 0);
+      if (j + 1 < n_body) tile(j + 1, 1);
+    }
+    if (n_loop > 0) {
+      const int j = n_loop - 1;
+      bar();
+      if (j < n_own) phase_x_last(VSLOT(j & 1));
+      bar();
+    }
   }
   if (grp == 0) bar();  // group A ends one phase earlier
 
