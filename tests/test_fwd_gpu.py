@@ -109,6 +109,40 @@ def test_pair_workgroups_mixed_head_layouts(hq, hkv, causal):
         check_o_lse(o, lse, o_ref, lse_ref, "bf16", f"H {hq}/{hkv} rank {r}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(260, 130), (264, 66)])
+def test_shared_tile_counts(d, hq, hkv):
+    """Pair workgroups whose two heads read one key/value head (GQA groups 2 and 4: the tiles are
+    loaded once for both groups and cycle through three slots), at every key-tile count from 1
+    to 10 (full and ragged last tile), so that the loop unrolled by three ends after each of its
+    three bodies; non-causal, and causal with the diagonal inside the chunk. One 128-row query
+    tile of 130 or 132 head pairs: more than half the chip's CUs, so no pair is split. The first
+    and last eight heads are compared with the oracle."""
+    lq = 128
+    g = hq // hkv
+    heads = list(range(8)) + list(range(hq - 8, hq))
+    kvh = sorted({h // g for h in heads})
+    qa = inputs.make(108, "q", d, (hq, lq, d), "bf16")
+    q = inputs.to_torch(qa, "cuda")
+    qs = inputs.widen(qa)[heads]
+    for n_tiles in range(1, 11):
+        for lk in (64 * n_tiles, 64 * n_tiles - 17):
+            ka = inputs.make(108, "k", lk, (hkv, lk, d), "bf16")
+            va = inputs.make(108, "v", lk, (hkv, lk, d), "bf16")
+            k, v = inputs.to_torch(ka, "cuda"), inputs.to_torch(va, "cuda")
+            ks, vs = inputs.widen(ka)[kvh], inputs.widen(va)[kvh]
+            for causal in (False, True):
+                q0 = max(0, lk - lq) if causal else 0
+                o_ref, lse_ref = oracle.attention_forward(qs, ks, vs, q_pos0=q0, kv_pos0=0,
+                                                          causal=causal)
+                o = torch.full((hq, lq, d), 7.0, device="cuda")
+                lse = torch.full((hq, lq), 7.0, device="cuda")
+                st = cp.step(q, k, v, o, lse, q_pos0=q0, kv_pos0=0, causal=causal)
+                assert st == cp.CP_OK
+                check_o_lse(o[heads].cpu().numpy(), lse[heads].cpu().numpy(), o_ref, lse_ref,
+                            "bf16", f"d {d} H {hq}/{hkv} keys {lk} causal {causal}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("q0,k0,causal,accumulate", [
     (0, 0, True, False),      # diagonal
