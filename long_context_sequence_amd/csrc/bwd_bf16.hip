@@ -213,6 +213,41 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* sme
   const int dpos = causal_shift(p.q_pos0, p.kv_pos0);
   const int wave_key0 = kv_base + 32 * kwave;  // first key of the wave
 
+  // Byte offsets of this lane's operand reads inside a tile. The swizzle of a row depends only on
+  // its low four bits, so they are the same for every tile, buffer and 16-row step: computed
+  // once and kept in registers (the empty asm keeps the compiler from recomputing the swizzle
+  // in the loop); a read then costs one add for the buffer, the block being an immediate.
+  uint32_t off_row[KS];  // row operand: row perm_row(col) of a 32-row block, chunk 2 ks + half
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    off_row[ks] = 2u * (uint32_t)tile_off<D>(perm_row(col), 2 * ks + half);
+    asm volatile("" : "+v"(off_row[ks]));
+  }
+  uint32_t off_tr[2][NB];  // transposed operand (two reads): column block m of a 16-row step
+  {
+    const int g16 = lane >> 4, li = lane & 15;
+    const int rr = 8 * (g16 >> 1) + (li >> 2);
+#pragma unroll
+    for (int m = 0; m < NB; ++m) {
+      const int cx = 32 * m + 16 * (g16 & 1) + 4 * (li & 3);
+      off_tr[0][m] = 2u * (uint32_t)(tile_off<D>(rr, cx >> 3) + (cx & 7));
+      off_tr[1][m] = 2u * (uint32_t)(tile_off<D>(rr + 4, cx >> 3) + (cx & 7));
+      asm volatile("" : "+v"(off_tr[0][m]), "+v"(off_tr[1][m]));
+    }
+  }
+  auto rd_row = [&](const uint16_t* tile, int b, int ks) {
+    return *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(tile) +
+                                             off_row[ks] + 64 * D * b);
+  };
+  auto rd_tr = [&](const uint16_t* tile, int r0, int m) {  // rows r0 .. r0 + 15, r0 % 16 == 0
+    const char* t = reinterpret_cast<const char*>(tile) + 2 * r0 * D;
+    const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(t + off_tr[0][m]));
+    const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(t + off_tr[1][m]));
+    const u32x2_t w0 = __builtin_bit_cast(u32x2_t, v0);
+    const u32x2_t w1 = __builtin_bit_cast(u32x2_t, v1);
+    return u32x4_t{w0[0], w0[1], w1[0], w1[1]};
+  };
+
   for (int it = 0; it < n_it; ++it) {
     const int buf = it & 1;
     float stg = 0.f;
@@ -222,7 +257,6 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* sme
     // One 32-row block of the tile against the wave's 32 keys, in three steps:
     // chains: S = Q K^T (and dP = dO V^T) on the matrix cores;
     auto chains = [&](int b, f32x16_t& s, f32x16_t& dp, auto pf) {
-      const int arow = 32 * b + perm_row(col);
       s = f32x16_t{};
       dp = f32x16_t{};
       if constexpr (!DV) {
@@ -236,8 +270,8 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* sme
         }
       }
       mfma_chains<KS, decltype(pf)::value, !DV>(
-          [&](int ks) { return tile_row8<D>(SQ(buf), arow, 2 * ks + half); },
-          [&](int ks) { return tile_row8<D>(SDO(buf), arow, 2 * ks + half); }, kb, vb, s, dp);
+          [&](int ks) { return rd_row(SQ(buf), b, ks); },
+          [&](int ks) { return rd_row(SDO(buf), b, ks); }, kb, vb, s, dp);
     };
     // soft: P = exp2(S*c - lse2) (dV part) or dS = P (dP - delta) (dK part), to bf16;
     auto soft = [&](int b, const f32x16_t& s, const f32x16_t& dp, bool need_mask,
@@ -263,7 +297,7 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* sme
     auto accum = [&](int b, const u32x4_t (&pb)[2]) {
       const uint16_t* tt = DV ? SDO(buf) : SQ(buf);
       mfma_pipe<2 * NB, CP_BWD_PF_ACC>(
-          [&](int i) { return tile_col8<D>(tt, 32 * b + 16 * (i / NB), 32 * (i % NB), lane); },
+          [&](int i) { return rd_tr(tt, 32 * b + 16 * (i / NB), i % NB); },
           [&](int i, const u32x4_t& a) { acc[i % NB] = mfma32x32x16(a, pb[i / NB], acc[i % NB]); });
     };
     auto do_block = [&](int b, bool need_mask) {
@@ -281,8 +315,8 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* sme
         f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{}, unused = f32x16_t{};
         u32x4_t pb0[2], pb1[2];
         mfma_chains<KS, CP_BWD_PF_KV, true>(
-            [&](int ks) { return tile_row8<D>(SQ(buf), perm_row(col), 2 * ks + half); },
-            [&](int ks) { return tile_row8<D>(SQ(buf), 32 + perm_row(col), 2 * ks + half); }, kb,
+            [&](int ks) { return rd_row(SQ(buf), 0, ks); },
+            [&](int ks) { return rd_row(SQ(buf), 1, ks); }, kb,
             kb, s0, s1);
         soft(0, s0, unused, false, pb0);
         soft(1, s1, unused, false, pb1);
