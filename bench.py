@@ -467,9 +467,12 @@ def cpu_baseline(pool, n_workers, wl, rank, budget_s, with_bwd):
     visible = rank * lc + lc // 2 if wl.causal else wl.seq_len
     rows = int(max(16, min(lc, budget_s * 12e9 / (per_pair * visible))))
     rng = np.random.default_rng(0)
-    tasks = [(wl.key, rank, int(rng.integers(0, wl.heads_q)), int(rng.integers(0, lc - rows + 1)),
-              rows, with_bwd) for _ in range(n_workers)]
-    pool.map(_oracle_block, [(wl.key, rank, t[2], 0, 1, False) for t in tasks])  # warm inputs
+    # heads of one key/value group, so that every worker needs the same K and V (generated once
+    # per worker by the warm-up map, outside the timed region)
+    g = int(rng.integers(0, wl.heads_kv))
+    tasks = [(wl.key, rank, g * wl.group + i % wl.group, int(rng.integers(0, lc - rows + 1)),
+              rows, with_bwd) for i in range(n_workers)]
+    pool.map(_oracle_block, [(wl.key, rank, t[2], 0, 1, False) for t in tasks], chunksize=1)
     t0 = time.perf_counter()
     res = pool.map(_oracle_block, tasks, chunksize=1)
     wall = time.perf_counter() - t0
