@@ -52,6 +52,11 @@ constexpr int kRows = 128;    // query rows per group (32 per wave)
 constexpr int kPF = CP_FWD_PF;
 constexpr float kTau = 8.f;   // the reference max moves only when a row max grows by more than
                               // this (log2 units): P stays <= 2^8 and most tiles skip the rescale
+// A tile whose P, against the current reference, sum to at most this has every P below 2^kTau
+// (a rounded sum of non-negative terms is never below its largest term), so its row max cannot
+// have outgrown the reference by more than kTau.
+constexpr float kSumFast = 255.f;
+static_assert(kTau == 8.f, "kSumFast must stay below 2^kTau");
 
 // LDS of one group: K slots 0, 1 then V slots 0, 1, one 64 x D bf16 tile each.
 template <int D>
@@ -233,36 +238,49 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(StepParams p, int n_pa
           sc[blk][r] = vis ? sc[blk][r] : -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    // P = exp2(s*c2 - m) against reference max m, packed to bf16 pairs; returns the row sum.
+    auto exps = [&](float m_use) __attribute__((always_inline)) -> float {
+      float ls = 0.f;
 #pragma unroll
-    for (int blk = 0; blk < SB; ++blk)
+      for (int blk = 0; blk < SB; ++blk)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[blk][r]);
-    mx = pair_max(mx) * c2;
-    // Move the reference max only when the row max outgrew it by more than kTau (the first
-    // visible tile always does: m_run starts at -inf). P = exp2(s*c2 - m_run) <= 2^kTau.
-    const bool grow = mx > m_run + kTau;
-    const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
-    m_run = grow ? mx : m_run;
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+          for (int t = 0; t < 4; ++t) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[blk][8 * q + 2 * t], c2, -m_use));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[blk][8 * q + 2 * t + 1], c2, -m_use));
+            pb[2 * blk + q][t] = pack_bf16x2(p0, p1);
+            ls += p0 + p1;
+          }
+      return ls;
+    };
+    // First against the current reference max. A row sum of at most kSumFast bounds every P of
+    // the row below 2^kTau, so the reference stays, exactly as the row-max test below would
+    // decide, and the row max is never needed. A larger sum, or inf / NaN (no reference yet:
+    // m_run = -inf), sends the wave through that test.
+    float alpha = 1.f;
+    float lsum = exps(m_run);
+    if (__builtin_amdgcn_ballot_w64(!(lsum <= kSumFast)) != 0) {
+      float mx = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[nb][r] *= alpha;
+      for (int blk = 0; blk < SB; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[blk][r]);
+      mx = pair_max(mx) * c2;
+      // Move the reference max only when the row max outgrew it by more than kTau (the first
+      // visible tile always does: m_run starts at -inf). P = exp2(s*c2 - m_run) <= 2^kTau.
+      const bool grow = mx > m_run + kTau;
+      alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
+      m_run = grow ? mx : m_run;
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[nb][r] *= alpha;
+      }
+      lsum = exps(m_use);
     }
-    float lsum = 0.f;
-#pragma unroll
-    for (int blk = 0; blk < SB; ++blk)
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[blk][8 * q + 2 * t], c2, -m_use));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[blk][8 * q + 2 * t + 1], c2, -m_use));
-          pb[2 * blk + q][t] = pack_bf16x2(p0, p1);
-          lsum += p0 + p1;
-        }
     l_run = l_run * alpha + lsum;
   };
   // Workgroup barrier between phases; the scheduling fences keep each phase's instructions on
