@@ -254,10 +254,11 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(StepParams p, int n_pa
           }
       return ls;
     };
-    // First against the current reference max. A row sum of at most kSumFast bounds every P of
-    // the row below 2^kTau, so the reference stays, exactly as the row-max test below would
-    // decide, and the row max is never needed. A larger sum, or inf / NaN (no reference yet:
-    // m_run = -inf), sends the wave through that test.
+    // First against the current reference max. A lane's sum (its half of the row's 64 P) of at
+    // most kSumFast bounds every P it holds below 2^kTau; when that holds in every lane the
+    // reference stays, exactly as the row-max test below would decide, and the row max is never
+    // needed. A larger sum, or inf / NaN (no reference yet: m_run = -inf), in any lane sends the
+    // wave through that test.
     float alpha = 1.f;
     float lsum = exps(m_run);
     if (__builtin_amdgcn_ballot_w64(!(lsum <= kSumFast)) != 0) {
