@@ -143,6 +143,65 @@ def test_shared_tile_counts(d, hq, hkv):
                             "bf16", f"d {d} H {hq}/{hkv} keys {lk} causal {causal}")
 
 
+def _crafted_keys(case, hkv, lk, d):
+    """Keys that move the softmax's reference max in controlled ways, tile by tile (64 keys).
+
+    growing: N(0,1) rows scaled by 1 + 4t on key tile t, so every tile's row max outgrows the
+             previous one by far more than the rescale threshold (2^8 in P);
+    plateau: every query row is 0.125 * ones and the keys of tile t are b_t * 0.125 * ones, with
+             s * scale * log2(e) = 0, then ~3, then ~3 again: the second tile's P are ~8 each, so a
+             lane's 32 P sum past 255 while the max grows by less than the threshold (the
+             reference must stay), and the third tile repeats the same scores;
+    jump:    N(0,1) rows, scaled by 8 from the middle tile on (one large move mid-row)."""
+    rng = np.random.default_rng(11)
+    t = np.arange(lk) // 64
+    if case == "growing":
+        k = rng.standard_normal((hkv, lk, d)).astype(np.float32) * (1 + 4 * t)[None, :, None]
+    elif case == "jump":
+        k = rng.standard_normal((hkv, lk, d)).astype(np.float32)
+        k[:, lk // 2:] *= 8.0
+    else:
+        c2 = (1.0 / np.sqrt(d)) * np.log2(np.e)
+        unit = np.float32(0.125)
+        b = np.where(t == 0, 0.0, 3.0 / (d * unit * unit * c2)).astype(np.float32)
+        k = np.broadcast_to((b[:, None] * unit)[None], (hkv, lk, d)).astype(np.float32).copy()
+    return inputs.bf16_rne_bits(k)
+
+
+@pytest.mark.parametrize("case", ["growing", "plateau", "jump"])
+@pytest.mark.parametrize("hq,hkv,d", [(260, 130, 128), (130, 130, 128), (260, 130, 64)])
+def test_softmax_reference_moves(case, hq, hkv, d):
+    """The forward's running max on inputs that move it: every tile (growing), never past the
+    threshold although the tile's P sum past the fast-path bound (plateau), once by a large step
+    (jump). Shared-tile pairs (group 2) and separate-tile pairs (MHA), one 128-row query tile, so
+    no pair is split; three key-tile counts, causal and not. First and last eight heads against
+    the oracle."""
+    lq = 128
+    g = hq // hkv
+    heads = list(range(8)) + list(range(hq - 8, hq))
+    kvh = sorted({h // g for h in heads})
+    if case == "plateau":
+        qa = inputs.bf16_rne_bits(np.full((hq, lq, d), 0.125, dtype=np.float32))
+    else:
+        qa = inputs.make(109, "q", d, (hq, lq, d), "bf16")
+    q = inputs.to_torch(qa, "cuda")
+    qs = inputs.widen(qa)[heads]
+    for lk in (192, 320, 448):
+        ka = _crafted_keys(case, hkv, lk, d)
+        va = inputs.make(109, "v", lk, (hkv, lk, d), "bf16")
+        k, v = inputs.to_torch(ka, "cuda"), inputs.to_torch(va, "cuda")
+        ks, vs = inputs.widen(ka)[kvh], inputs.widen(va)[kvh]
+        for causal in (False, True):
+            q0 = lk - lq if causal else 0
+            o_ref, lse_ref = oracle.attention_forward(qs, ks, vs, q_pos0=q0, kv_pos0=0,
+                                                      causal=causal)
+            o = torch.full((hq, lq, d), 7.0, device="cuda")
+            lse = torch.full((hq, lq), 7.0, device="cuda")
+            assert cp.step(q, k, v, o, lse, q_pos0=q0, kv_pos0=0, causal=causal) == cp.CP_OK
+            check_o_lse(o[heads].cpu().numpy(), lse[heads].cpu().numpy(), o_ref, lse_ref, "bf16",
+                        f"{case} d {d} H {hq}/{hkv} keys {lk} causal {causal}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("q0,k0,causal,accumulate", [
     (0, 0, True, False),      # diagonal
