@@ -202,6 +202,7 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(StepParams p, int n_pa
     sc[i % SB] = mfma32x32x16(a, qreg[i / SB], sc[i % SB]);
   };
   constexpr int NPV = 2 * SB * NB, NS = KS * SB;
+  constexpr int kMove = NPV / 4;  // PV products of the last 16-key step
   auto zero_s = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int blk = 0; blk < SB; ++blk) sc[blk] = f32x16_t{};
@@ -211,16 +212,28 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(StepParams p, int n_pa
   auto phase_x = [&](const uint16_t* __restrict__ v_rd, const uint16_t* __restrict__ k_rd) __attribute__((always_inline)) {
     zero_s();
     if (CP_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
-    // PV and S products alternate: S has two accumulators, and a product must not follow the
-    // product that accumulates into the same registers too closely.
-    static_assert(NPV == NS, "alternating PV and S products");
-    mfma_seq<NPV + NS, kPF>(
-        [&](int i) { return (i & 1) == 0 ? pv_load(v_rd, i / 2) : s_load(k_rd, i / 2); },
+    // Products in groups of seven, S PV S PV S PV S: S has two accumulators, and a product must
+    // not follow the product that accumulates into the same registers too closely. The PV
+    // products of the tile's last 16-key step run at the start of Y_j instead (pv_tail), which
+    // balances the two phases.
+    static_assert(NPV == NS && NS % 4 == 0, "groups of four S and three PV products");
+    mfma_seq<NS + NPV - kMove, kPF>(
+        [&](int i) {
+          const int g7 = i / 7, r7 = i % 7;
+          return (r7 & 1) == 0 ? s_load(k_rd, 4 * g7 + r7 / 2) : pv_load(v_rd, 3 * g7 + r7 / 2);
+        },
         [&](int i, const u32x4_t& a) {
-          if ((i & 1) == 0) pv_step(i / 2, a);
-          else s_step(i / 2, a);
+          const int g7 = i / 7, r7 = i % 7;
+          if ((r7 & 1) == 0) s_step(4 * g7 + r7 / 2, a);
+          else pv_step(3 * g7 + r7 / 2, a);
         });
     if (CP_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
+  };
+  // The PV products X_j left out: O^T += V_j^T P_j over the tile's last 16 keys (before Y_j
+  // overwrites those P).
+  auto pv_tail = [&](const uint16_t* __restrict__ v_rd) __attribute__((always_inline)) {
+    mfma_seq<kMove, 2>([&](int i) { return pv_load(v_rd, NPV - kMove + i); },
+                           [&](int i, const u32x4_t& a) { pv_step(NPV - kMove + i, a); });
   };
   // Phase Y_j: softmax of S_{j+1}: mask, running max (lazy rescale of O and the sum), P to bf16.
   auto phase_y = [&](int j) __attribute__((always_inline)) {
@@ -339,6 +352,7 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(StepParams p, int n_pa
         else wait_vmcnt<0>();
       }
       bar();
+      pv_tail(VSH(s));
       phase_y(j);
       if (grp == 0) {  // K_{j+2} complete; K_{j+3} may stay in flight
         if (j + 3 < n) wait_vmcnt<Dma::ITERS>();
@@ -379,6 +393,7 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(StepParams p, int n_pa
       if (j + 1 < n_own) load_v(j + 1, VSLOT(1 - s));
       if (j < n_own) phase_x(VSLOT(s), KSLOT(1 - s));
       bar();
+      if (j < n_own) pv_tail(VSLOT(s));
       phase_y(j);
       __builtin_amdgcn_s_waitcnt(0);
     };

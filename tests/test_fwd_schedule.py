@@ -2,18 +2,20 @@
 `shared` branch): two groups of four wavefronts, group B one phase behind group A, a workgroup
 barrier between phases, three K and three V slots in LDS, tile t in slot t % 3. Group A loads
 the K tiles, group B the V tiles; each group waits for its loads with a vmcnt that leaves its
-newest load in flight.
+newest load in flight. V_j is read in both phases of tile j: the matrix phase X_j and, for the
+PV products of the tile's last 16 keys, the start of the softmax phase Y_j.
 
 The model replays both groups' program order (loads, waits, LDS reads, barriers) for 0..60 tiles
 and checks, for every read of a tile: its load was issued into that slot, completed by the
 issuing group's wait and published by a later barrier; and no load of a later tile into the same
 slot was issued in or before the read's phase. Both groups pass the same number of barriers.
-Planted mistakes (a wrong slot, a wait that leaves one load too many in flight) must fail.
+Planted mistakes (a wrong slot, a wait that leaves one load too many in flight, the softmax
+phase's V read from the wrong slot) must fail.
 """
 import pytest
 
 
-def _program(grp, n, bad_slot=False, bad_wait=False):
+def _program(grp, n, bad_slot=False, bad_wait=False, bad_tail=False):
     ev = []
     bar = lambda: ev.append(("bar",))
     if grp == 0:
@@ -47,6 +49,8 @@ def _program(grp, n, bad_slot=False, bad_wait=False):
         if grp == 1:
             ev.append(("wait", keep if j + 2 < n else 0))
         bar()
+        # the PV products of the tile's last 16 keys run at the start of Y_j
+        ev.append(("read", "V", j, (s + 1) % 3 if (bad_tail and j > 4) else s))
         if grp == 0:
             ev.append(("wait", keep if j + 3 < n else 0))
 
@@ -104,7 +108,7 @@ def test_shared_tile_schedule(n):
     _check(n)
 
 
-@pytest.mark.parametrize("plant", [{"bad_slot": True}, {"bad_wait": True}])
+@pytest.mark.parametrize("plant", [{"bad_slot": True}, {"bad_wait": True}, {"bad_tail": True}])
 def test_planted_schedule_mistakes_fail(plant):
     with pytest.raises(AssertionError):
         for n in range(0, 61):
