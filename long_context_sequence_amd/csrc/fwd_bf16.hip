@@ -166,6 +166,23 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(StepParams p, int n_pa
   const int wave_row0 = it.q_base + 32 * wave;
   const int n_own = active ? it.n_tiles : 0;
 
+  // The running (O, LSE) that the epilogue folds this step into, fetched before the last tile's
+  // products so that the loads overlap them (only the lanes that fold: group B of a split
+  // workgroup hands its partial to group A instead).
+  f32x4_t o_old[4 * NB];
+  float lse_old = -INFINITY;
+  const bool folds = p.accumulate && q_ok && n_own > 0 && !(split && grp == 1);
+  auto fetch_old = [&]() __attribute__((always_inline)) {
+    if (!folds) return;
+    const float* orow = p.o + ((size_t)it.h * p.len_q + qi) * D;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4)
+        o_old[4 * nb + a4] = *reinterpret_cast<const f32x4_t*>(orow + 32 * nb + 8 * a4 + 4 * half);
+    lse_old = p.lse[(size_t)it.h * p.len_q + qi];
+  };
+
   using Dma = TileDma<D, kBN, 256>;
   // Direct loads of tile t (keys key_lo + 64 t ...) of K or V into a slot.
   auto load_k = [&](int t, uint16_t* slot) __attribute__((always_inline)) {
@@ -367,6 +384,7 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(StepParams p, int n_pa
       }
     }
     if (n > 0) {
+      fetch_old();
       bar();
       phase_x_last(VSH((n - 1) % 3));
       bar();
@@ -403,6 +421,7 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(StepParams p, int n_pa
     }
     if (n_loop > 0) {
       const int j = n_loop - 1;
+      fetch_old();
       bar();
       if (j < n_own) phase_x_last(VSLOT(j & 1));
       bar();
@@ -463,7 +482,6 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(StepParams p, int n_pa
   } else if (lse_new != -INFINITY) {
     // Fold into the running (O, LSE): LSE' = logaddexp(old, new), weights exp(old - LSE') and
     // exp(new - LSE').
-    const float lse_old = *lrow;
     const float hi = fmaxf(lse_old, lse_new);
     const float lse_m = hi + log1pf(expf(-fabsf(lse_old - lse_new)));
     const float wa = expf(lse_old - lse_m);
@@ -473,7 +491,7 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(StepParams p, int n_pa
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         f32x4_t* ptr = reinterpret_cast<f32x4_t*>(orow + 32 * nb + 8 * a4 + 4 * half);
-        const f32x4_t old = *ptr;
+        const f32x4_t old = o_old[4 * nb + a4];
         f32x4_t v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = wa * old[e] + wb * oacc[nb][4 * a4 + e];
