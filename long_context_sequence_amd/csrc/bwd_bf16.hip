@@ -109,7 +109,8 @@ constexpr int kPartDV = 1, kPartDK = 2;
 // LDS of the kv parts: Q and dO tiles, double buffered, then LSE*log2e and delta per row.
 template <int D>
 constexpr int kv_smem_bytes() { return 2 * 2 * kQT * D * 2 + 2 * 2 * kQT * 4; }
-// LDS of the dQ part: K and V tiles, double buffered.
+// LDS of the dQ part: K and V tiles, double buffered (one such region per group of a split
+// dQ workgroup).
 template <int D>
 constexpr int dq_smem_bytes() { return 2 * 2 * kKT * D * 2; }
 
@@ -356,26 +357,36 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, int w, char* sme
     }
 }
 
-template <int D, int NW>
+// SPLIT (8-wave workgroups only): the workgroup takes half of work item w / 2, rows
+// [128 (w % 2), 128 (w % 2) + 128) of its 256, and its two groups of four waves split the keys:
+// group A the first ceil(n/2) tiles, group B the rest, each streaming its own tiles through its
+// own LDS region; B hands its partial dQ to A through LDS at the end. Such workgroups take half
+// as long, and the launch ends with them.
+template <int D, int NW, bool SPLIT = false>
 __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int w, char* smem) {
+  static_assert(!SPLIT || NW == 8, "a split dQ workgroup is two groups of four waves");
   constexpr int KS = D / 16, NB = D / 32, BM = 32 * NW;
-  uint16_t* const sk_base = reinterpret_cast<uint16_t*>(smem);
+  constexpr int RW = SPLIT ? 4 : NW;  // waves that share the key tiles (and own the rows)
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int wave = tid >> 6;
+  const int grp = SPLIT ? __builtin_amdgcn_readfirstlane(wave >> 2) : 0;  // wave-uniform
+  const int wv = SPLIT ? wave & 3 : wave;  // wave within the group
+  uint16_t* const sk_base = reinterpret_cast<uint16_t*>(smem) + grp * (4 * kKT * D);
   uint16_t* const sv_base = sk_base + 2 * kKT * D;
   auto SK = [&](int b) { return sk_base + b * (kKT * D); };
   auto SV = [&](int b) { return sv_base + b * (kKT * D); };
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, half = lane >> 5, col = lane & 31;
-  const int wave = tid >> 6;
+  const int u = SPLIT ? w >> 1 : w;  // work item of 256 (8 waves) or 128 (4 waves) rows
   const int n_qt = (p.len_q + BM - 1) / BM;
-  const int h_in = w % p.group;
-  const int rest = w / p.group;
+  const int h_in = u % p.group;
+  const int rest = u / p.group;
   const int qt = n_qt - 1 - rest % n_qt;  // causally longest tiles first
   const int g = rest / n_qt;
   const int h = g * p.group + h_in;
-  const int q_base = qt * BM;
+  const int q_base = qt * BM + (SPLIT ? 32 * RW * (w & 1) : 0);
 
-  const int qi = q_base + 32 * wave + col;
+  const int qi = q_base + 32 * wv + col;
   const bool q_ok = qi < p.len_q;
   const int qi_c = q_ok ? qi : p.len_q - 1;
   const uint16_t* qh = static_cast<const uint16_t*>(p.q) + (size_t)h * p.len_q * D;
@@ -392,29 +403,34 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int w, char* sme
   const float lse2 = lse_raw == -INFINITY ? INFINITY : lse_raw * kLog2e;
   const float del = q_ok ? p.delta[(size_t)h * p.len_q + qi] : 0.f;
 
-  const int last_row = min(q_base + BM, p.len_q) - 1;
+  const int last_row = min(q_base + 32 * RW, p.len_q) - 1;
   long long nk = p.len_kv;
   if (p.causal) nk = min(nk, p.q_pos0 + last_row - p.kv_pos0 + 1);
   const int n_kt = nk > 0 ? (int)((nk + kKT - 1) / kKT) : 0;
+  // This group's key tiles [kt0, kt_end); a split workgroup's groups step through n_steps
+  // tiles each (group B idles through the last one when n_kt is odd).
+  const int n_steps = SPLIT ? (n_kt + 1) / 2 : n_kt;
+  const int kt0 = grp == 0 ? 0 : n_steps;
+  const int kt_end = grp == 0 ? n_steps : n_kt;
 
   const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (size_t)g * p.len_kv * D;
   const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (size_t)g * p.len_kv * D;
-  using Dma = TileDma<D, kKT, 64 * NW>;
+  using Dma = TileDma<D, kKT, 64 * RW>;
 
   f32x16_t dqt[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) dqt[nb] = f32x16_t{};
 
-  if (n_kt > 0) {
-    Dma::issue(kg, 0, p.len_kv, SK(0), wave, lane);
-    Dma::issue(vg, 0, p.len_kv, SV(0), wave, lane);
+  if (kt0 < kt_end) {
+    Dma::issue(kg, kt0 * kKT, p.len_kv, SK(0), wv, lane);
+    Dma::issue(vg, kt0 * kKT, p.len_kv, SV(0), wv, lane);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   const float c2 = p.scale_log2;
   const int dpos = causal_shift(p.q_pos0, p.kv_pos0);
-  const int wave_row0 = q_base + 32 * wave;
+  const int wave_row0 = q_base + 32 * wv;
 
   // Key tiles that every row of the workgroup sees in full (and that lie inside the chunk) come
   // first: they run without any mask code. The rest (the diagonal and the ragged end) follow.
@@ -425,14 +441,14 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int w, char* sme
   }
   n_full = min(n_full, n_kt);
 
-  // `bufc` = kt % 2 as a compile-time constant where the caller knows it (then every LDS address
-  // of the tile is a per-lane base plus an immediate offset), or -1.
+  // `bufc` = (kt - kt0) % 2 as a compile-time constant where the caller knows it (then every
+  // LDS address of the tile is a per-lane base plus an immediate offset), or -1.
   auto tile = [&](int kt, auto fullc, auto bufc) {
     constexpr bool kFull = decltype(fullc)::value;
-    const int buf = decltype(bufc)::value < 0 ? (kt & 1) : decltype(bufc)::value;
-    if (kt + 1 < n_kt) {
-      Dma::issue(kg, (kt + 1) * kKT, p.len_kv, SK(buf ^ 1), wave, lane);
-      Dma::issue(vg, (kt + 1) * kKT, p.len_kv, SV(buf ^ 1), wave, lane);
+    const int buf = decltype(bufc)::value < 0 ? ((kt - kt0) & 1) : decltype(bufc)::value;
+    if (kt + 1 < kt_end) {
+      Dma::issue(kg, (kt + 1) * kKT, p.len_kv, SK(buf ^ 1), wv, lane);
+      Dma::issue(vg, (kt + 1) * kKT, p.len_kv, SV(buf ^ 1), wv, lane);
     }
     const int key0 = kt * kKT;
     // One 32-key block of the tile against the wave's 32 query rows.
@@ -484,12 +500,38 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int w, char* sme
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-  int kt = 0;
-  for (; kt + 1 < n_full; kt += 2) {  // unrolled by two: the buffer index is a constant
-    tile(kt, std::true_type{}, std::integral_constant<int, 0>{});
-    tile(kt + 1, std::true_type{}, std::integral_constant<int, 1>{});
+  if constexpr (!SPLIT) {
+    int kt = 0;
+    for (; kt + 1 < n_full; kt += 2) {  // unrolled by two: the buffer index is a constant
+      tile(kt, std::true_type{}, std::integral_constant<int, 0>{});
+      tile(kt + 1, std::true_type{}, std::integral_constant<int, 1>{});
+    }
+    for (; kt < n_kt; ++kt) tile(kt, std::bool_constant<false>{}, std::integral_constant<int, -1>{});
+  } else {
+    const int cnt = kt_end - kt0;
+    const int nf = max(0, min(cnt, n_full - kt0));  // this group's mask-free tiles come first
+    int i = 0;
+    for (; i + 1 < nf; i += 2) {
+      tile(kt0 + i, std::true_type{}, std::integral_constant<int, 0>{});
+      tile(kt0 + i + 1, std::true_type{}, std::integral_constant<int, 1>{});
+    }
+    for (; i < cnt; ++i) tile(kt0 + i, std::bool_constant<false>{}, std::integral_constant<int, -1>{});
+    for (; i < n_steps; ++i) __syncthreads();  // group B, one tile fewer: keeps step with A
+    // B's partial dQ^T goes to A through LDS (the tiles are no longer read), lane-contiguous.
+    float* const xch = reinterpret_cast<float*>(smem) + wv * (16 * NB) * 64;
+    if (grp == 1) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xch[(16 * nb + r) * 64 + lane] = dqt[nb][r];
+    }
+    __syncthreads();
+    if (grp == 1) return;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dqt[nb][r] += xch[(16 * nb + r) * 64 + lane];
   }
-  for (; kt < n_kt; ++kt) tile(kt, std::bool_constant<false>{}, std::integral_constant<int, -1>{});
 
   if (!q_ok) return;
   float* dqr = p.dq + ((size_t)h * p.len_q + qi) * D;
@@ -506,13 +548,16 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, int w, char* sme
 }
 
 // One launch per ring step: the dK part's workgroups first (the longest), then the dV part's,
-// then the dQ kernel's, so that the short dQ workgroups fill the tail left by the others. The
-// three bodies share one LDS buffer; n_dk, n_dv, n_dq are the segment sizes (0 = segment off).
-// With NW = 8 the first segment holds the mixed dK/dV workgroups and the second is empty.
+// then the dQ kernel's, so that the short dQ workgroups fill the tail left by the others, and
+// last the split dQ workgroups (8-wave launches), which take half as long again and so even out
+// the launch's end. The bodies share one LDS buffer; n_dk, n_dv, n_dq, n_dqs are the segment
+// sizes (0 = segment off). With NW = 8 the first segment holds the mixed dK/dV workgroups and
+// the second is empty.
 template <int D, int NW>
-__global__ void __launch_bounds__(64 * NW, 2) bwd_kernel(BwdParams p, int n_dk, int n_dv, int n_dq) {
-  constexpr int kSmem = kv_smem_bytes<D>() > dq_smem_bytes<D>() ? kv_smem_bytes<D>()
-                                                                 : dq_smem_bytes<D>();
+__global__ void __launch_bounds__(64 * NW, 2)
+    bwd_kernel(BwdParams p, int n_dk, int n_dv, int n_dq, int n_dqs) {
+  constexpr int kDq = (NW == 8 ? 2 : 1) * dq_smem_bytes<D>();
+  constexpr int kSmem = kv_smem_bytes<D>() > kDq ? kv_smem_bytes<D>() : kDq;
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
   int b = blockIdx.x;
   if (b < n_dk) {
@@ -533,37 +578,55 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_kernel(BwdParams p, int n_dk, 
     return;
   }
   b -= n_dv;
-  if (b < n_dq) bwd_dq_body<D, NW>(p, xcd_remap(b, n_dq), smem);
+  if (b < n_dq) {
+    bwd_dq_body<D, NW>(p, xcd_remap(b, n_dq), smem);
+    return;
+  }
+  b -= n_dq;
+  if constexpr (NW == 8) {
+    // halves of the work items that follow the n_dq whole ones
+    if (b < n_dqs) bwd_dq_body<D, NW, true>(p, 2 * n_dq + xcd_remap(b, n_dqs), smem);
+  }
 }
 
-// Workgroups of the launch at NW waves: {dK part, dV part, dQ part}.
+// Workgroups of the launch at NW waves: {dK part, dV part, dQ part, split dQ part}.
 struct BwdGrid {
-  int n_dk, n_dv, n_dq;
-  long long total() const { return (long long)n_dk + n_dv + n_dq; }
+  int n_dk, n_dv, n_dq, n_dqs;
+  long long total() const { return (long long)n_dk + n_dv + n_dq + n_dqs; }
 };
 BwdGrid bwd_grid(const BwdParams& p, int which, int nw) {
   const int rows = 32 * nw;
   const int n_q = ((p.len_q + rows - 1) / rows) * p.heads_q;
   if (nw == 8) {  // one workgroup per 128 keys for both parts
     const int n_mix = ((p.len_kv + 127) / 128) * p.heads_kv;
-    return {(which & 1) ? n_mix : 0, 0, (which & 2) ? n_q : 0};
+    return {(which & 1) ? n_mix : 0, 0, (which & 2) ? n_q : 0, 0};
   }
   const int n_kv = ((p.len_kv + rows - 1) / rows) * p.heads_kv;
-  return {(which & 1) ? n_kv : 0, (which & 1) ? n_kv : 0, (which & 2) ? n_q : 0};
+  return {(which & 1) ? n_kv : 0, (which & 1) ? n_kv : 0, (which & 2) ? n_q : 0, 0};
 }
 
 template <int D, int NW>
 hipError_t launch_dn(const BwdParams& p, const BwdGrid& g, hipStream_t s) {
   hipLaunchKernelGGL((bwd_kernel<D, NW>), dim3((unsigned)g.total()), dim3(64 * NW), 0, s, p,
-                     g.n_dk, g.n_dv, g.n_dq);
+                     g.n_dk, g.n_dv, g.n_dq, g.n_dqs);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const BwdParams& p, int which, hipStream_t s) {
-  const BwdGrid wide = bwd_grid(p, which, 8);
+  BwdGrid wide = bwd_grid(p, which, 8);
   if (wide.total() == 0) return hipSuccess;
-  if (wide.total() >= kWideGrid) return launch_dn<D, 8>(p, wide, s);
+  if (wide.total() >= kWideGrid) {
+    // When every key is visible to every row, all dQ work items take the same time and the
+    // launch would end on a ragged last round of them: the last round's worth (one item per
+    // CU) runs as split workgroups of half the length instead. (Under a causal mask the items
+    // are ordered longest first and the short ones already even out the end.)
+    const bool uniform = !p.causal || p.kv_pos0 + p.len_kv - 1 <= p.q_pos0;
+    const int tail = uniform ? min(wide.n_dq, device_cus()) : 0;
+    wide.n_dq -= tail;
+    wide.n_dqs = 2 * tail;
+    return launch_dn<D, 8>(p, wide, s);
+  }
   return launch_dn<D, 4>(p, bwd_grid(p, which, 4), s);
 }
 

@@ -501,7 +501,8 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(StepParams p, int n_pa
   }
 }
 
-// Compute units of the current device (queried once per device).
+}  // namespace
+
 int device_cus() {
   static int cache[64] = {0};
   int dev = 0;
@@ -513,6 +514,8 @@ int device_cus() {
   if (dev < 64) cache[dev] = n;
   return n;
 }
+
+namespace {
 
 template <int D>
 hipError_t launch_d(const StepParams& p, hipStream_t s) {

@@ -40,6 +40,9 @@ struct BwdParams {
   float scale_log2;
 };
 
+// Compute units of the current device (queried once per device).
+int device_cus();
+
 hipError_t launch_fwd_bf16(const StepParams& p, hipStream_t s);
 hipError_t launch_fwd_f32(const StepParams& p, hipStream_t s);
 hipError_t launch_merge(long long rows, int head_dim, float* o_acc, float* lse_acc,

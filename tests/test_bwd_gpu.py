@@ -175,13 +175,15 @@ def _wide_grid_workgroups(hq, hkv, lc):
     return -(-lc // 128) * hkv + -(-lc // 256) * hq
 
 
-@pytest.mark.parametrize("d", [128, 64])
-def test_wide_grid_launch(d):
+@pytest.mark.parametrize("d,lc", [(128, 1000), (64, 1000), (128, 1050)])
+def test_wide_grid_launch(d, lc):
     """Backward launches large enough for 8-wavefront workgroups (the configuration of the
     208K shard), at a size the full oracle checks: 256 query heads over 128 key/value heads,
-    1000-row chunks (ragged against the 256-key and 256-row workgroups and the 64-row tiles),
-    rank 1 of 2 (one diagonal step, one fully visible step)."""
-    hq, hkv, lc = 256, 128, 1000
+    1000- or 1050-row chunks (ragged against the 256-key and 256-row workgroups and the 64-row
+    tiles), rank 1 of 2 (one diagonal step, one fully visible step). In the fully visible step
+    the last round of dQ work items runs as split workgroups (two groups of four wavefronts on
+    the two halves of the keys): 16 key tiles split evenly, 17 leave group B one tile short."""
+    hq, hkv = 256, 128
     assert _wide_grid_workgroups(hq, hkv, lc) >= 2048
     wl = small_workload(205, "bf16", hq, hkv, d, lc, 2, True, backward=True)
     r = 1
