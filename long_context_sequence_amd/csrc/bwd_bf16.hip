@@ -35,8 +35,9 @@ constexpr int kKT = 64;    // keys per tile (dq)
 constexpr int kWideGrid = 2048;
 
 // LDS operand reads issued ahead of their MFMA in the S/dP chains of the kv parts and of the
-// dQ part (0 = compiler's choice). Measured at the 208K shard: the dQ part gains ~7% at 2, the
-// kv parts lose ~5% at any depth.
+// dQ part (0 = compiler's choice). Measured on the 208K shard's backward ring: the dQ part
+// gains ~7% at 2; the kv parts of the 8-wave launch lose 3% at 0 and 0.5% at 4 against 2
+// (deeper dQ or accumulation prefetch spills registers).
 #ifndef CP_BWD_PF_KV
 #define CP_BWD_PF_KV 2
 #endif
