@@ -204,8 +204,8 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(StepParams p, int n_pa
   // Phase X_j: O^T += V_j^T P_j (j >= 0), S_{j+1}^T = K_{j+1} Q^T. The products' LDS operands
   // are read kPF products ahead of their use, with scheduling fences keeping that order: one
   // wavefront per SIMD issues products in this phase, so nothing else hides the LDS latency.
-  // Product i < 16 is PV (16-key step i / 4, d block i % 4), i >= 16 is S (d step (i-16) / 2,
-  // key block (i-16) % 2).
+  // PV product i: 16-key step i / NB, d block i % NB; S product i: d step i / SB, 32-key block
+  // i % SB.
   auto pv_load = [&](const uint16_t* v_rd, int i) {
     return tile_col8<D>(v_rd, 16 * (i / NB), 32 * (i % NB), lane);
   };
@@ -219,7 +219,7 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(StepParams p, int n_pa
     sc[i % SB] = mfma32x32x16(a, qreg[i / SB], sc[i % SB]);
   };
   constexpr int NPV = 2 * SB * NB, NS = KS * SB;
-  constexpr int kMove = NPV / 4;  // PV products of the last 16-key step
+  constexpr int kMove = NB;  // PV products of the tile's last 16-key step (one per d block)
   auto zero_s = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int blk = 0; blk < SB; ++blk) sc[blk] = f32x16_t{};
